@@ -1,0 +1,235 @@
+"""Oracle against library routines, the skew trick, brute force and invariants.
+
+  [RPE]  "Relative Position Embeddings, in depth" (aicassindra.com)
+  [T5B]  "T5 Relative-Position Bias" (liminalml.com)
+  [DRPE] "DeBERTa > Relative Position Encoding" (mbrenndoerfer.com)
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+
+ATOL = 1e-10
+
+
+def _sdpa(q, k, v, mask=None, scale=None):
+    """torch's reference attention on the CPU in float64 (math path)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        t(q)[None, None], t(k)[None, None], t(v)[None, None],
+        attn_mask=None if mask is None else t(mask)[None, None], scale=scale)
+    return out[0, 0].numpy()
+
+
+def _rand(rng, *shape, s=1.0):
+    return rng.standard_normal(shape) * s
+
+
+def _mask_add(Lq, Lk, q_off=0, causal=False, n_valid=None):
+    m = np.zeros((Lq, Lk))
+    qpos = q_off + np.arange(Lq)[:, None]
+    kpos = np.arange(Lk)[None, :]
+    if causal:
+        m = np.where(kpos > qpos, -np.inf, m)
+    if n_valid is not None:
+        m = np.where(kpos >= n_valid, -np.inf, m)
+    return m
+
+
+# ---------------------------------------------------------------- reductions
+
+@pytest.mark.parametrize("causal,n_valid,q_off", [(False, None, 0), (True, None, 0),
+                                                  (False, 13, 0), (True, None, 40)])
+def test_zero_tables_reduce_to_plain_attention(causal, n_valid, q_off):
+    rng = np.random.default_rng(1)
+    Lq, Lk, d = 17, 23 if not causal else 17 + q_off, 16
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    mask = _mask_add(Lq, Lk, q_off, causal, n_valid)
+    want = _sdpa(q, k, v, mask, 1 / math.sqrt(d))
+    want_deb = _sdpa(q, k, v, mask, 1 / math.sqrt(3 * d))   # [RPE] DeBERTa: sqrt(3d)
+    common = dict(q_pos_offset=q_off, causal=causal, n_valid=n_valid)
+    got = oracle.relattn_forward_head(q, k, v, "t5", 0, np.zeros((32, 1)), **common)
+    np.testing.assert_allclose(got, want, atol=ATOL)
+    z = np.zeros((9, d))
+    got = oracle.relattn_forward_head(q, k, v, "shaw", 0, z, z, clip_k=4, **common)
+    np.testing.assert_allclose(got, want, atol=ATOL)
+    z = np.zeros((10, 1, d))
+    got = oracle.relattn_forward_head(q, k, v, "deberta", 0, z, z, clip_k=5, **common)
+    np.testing.assert_allclose(got, want_deb, atol=ATOL)
+
+
+@pytest.mark.parametrize("bidir", [True, False])
+def test_t5_equals_sdpa_with_dense_bias(bidir):
+    # [RPE] "Kernels and the KV cache": a dense float mask carrying the bias
+    # through the library's attention gives the same result.
+    rng = np.random.default_rng(2)
+    Lq, Lk, d, H, h = 40, 300, 32, 3, 2
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    table = _rand(rng, 32, H, s=0.5)
+    q_off = 200
+    idx = oracle.rel_index_matrices("t5", Lq, Lk, q_pos_offset=q_off, bidirectional=bidir)["idx"]
+    mask = table[idx, h] + _mask_add(Lq, Lk, q_off, causal=not bidir)
+    want = _sdpa(q, k, v, mask, 1 / math.sqrt(d))
+    got = oracle.relattn_forward_head(q, k, v, "t5", h, table, bidirectional=bidir,
+                                      q_pos_offset=q_off, causal=not bidir)
+    np.testing.assert_allclose(got, want, atol=ATOL)
+
+
+def test_t5_constant_table_is_invisible():
+    # softmax shift invariance: one constant per head changes nothing.
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 20, 8), _rand(rng, 20, 8), _rand(rng, 20, 8)
+    table = np.full((32, 2), 0.37)
+    got = oracle.relattn_forward_head(q, k, v, "t5", 1, table)
+    np.testing.assert_allclose(got, _sdpa(q, k, v, None, 1 / math.sqrt(8)), atol=ATOL)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_shaw_gather_equals_skew_path(causal):
+    # [RPE] "The skewing trick": the causal relative logits from the
+    # pad-reshape-slice trick equal the clipped gather; for the encoder the
+    # trick runs a second time on the mirrored problem.
+    rng = np.random.default_rng(4)
+    L, d, kc = 12, 8, 3
+    q, k, v = _rand(rng, L, d), _rand(rng, L, d), _rand(rng, L, d)
+    a_k = _rand(rng, 2 * kc + 1, d, s=0.5)
+    # E[r] embeds distance r - (L - 1)
+    E = np.stack([a_k[min(max(r - (L - 1), -kc), kc) + kc] for r in range(L)])
+    lower = oracle.skew(q @ E.T)
+    # mirrored problem: reversed queries, E'[r] embeds distance (L - 1) - r
+    Em = np.stack([a_k[min(max((L - 1) - r, -kc), kc) + kc] for r in range(L)])
+    upper = oracle.skew(q[::-1] @ Em.T)[::-1, ::-1]
+    rel = np.tril(lower) + np.triu(upper, 1)
+    scale = 1 / math.sqrt(d)
+    mask = rel * scale + _mask_add(L, L, causal=causal)
+    want = _sdpa(q, k, v, mask, scale)
+    zeros = np.zeros_like(a_k)
+    got = oracle.relattn_forward_head(q, k, v, "shaw", 0, a_k, zeros, clip_k=kc, causal=causal)
+    np.testing.assert_allclose(got, want, atol=ATOL)
+
+
+def test_shaw_equal_key_rows_invisible_and_value_rows_shift():
+    rng = np.random.default_rng(5)
+    L, d, kc = 15, 8, 2
+    q, k, v = _rand(rng, L, d), _rand(rng, L, d), _rand(rng, L, d)
+    base = _sdpa(q, k, v, _mask_add(L, L, causal=True), 1 / math.sqrt(d))
+    a_k = np.tile(_rand(rng, 1, d), (2 * kc + 1, 1))
+    c = _rand(rng, 1, d)
+    a_v = np.tile(c, (2 * kc + 1, 1))
+    got = oracle.relattn_forward_head(q, k, v, "shaw", 0, a_k, a_v, clip_k=kc, causal=True)
+    np.testing.assert_allclose(got, base + c, atol=ATOL)
+
+
+def test_shaw_uniform_attention_closed_form():
+    # Q = K = 0 gives uniform weights over visible keys, so the value-side
+    # term is the average of a_V rows over the clipped offsets seen.
+    rng = np.random.default_rng(6)
+    L, d, kc = 11, 4, 3
+    z = np.zeros((L, d))
+    v = _rand(rng, L, d)
+    a_k = _rand(rng, 2 * kc + 1, d)
+    a_v = _rand(rng, 2 * kc + 1, d)
+    got = oracle.relattn_forward_head(z, z, v, "shaw", 0, a_k, a_v, clip_k=kc, causal=True)
+    for i in range(L):
+        n = i + 1
+        want = v[: i + 1].mean(0)
+        counts = np.zeros(2 * kc + 1)
+        for off in range(-i, 1):
+            counts[max(off, -kc) + kc] += 1
+        want = want + (counts / n) @ a_v
+        np.testing.assert_allclose(got[i], want, atol=ATOL)
+
+
+def test_masking_independence():
+    # [T5B]: masking is checked on its own -- entries of masked keys must
+    # not influence anything.
+    rng = np.random.default_rng(7)
+    Lq, Lk, d = 9, 30, 8
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    q_off, n_valid = 12, 19     # visible: keys <= 12 + i and < 19
+    k2, v2 = k.copy(), v.copy()
+    k2[19:] = 1e3 * _rand(rng, Lk - 19, d)
+    v2[19:] = -7.0
+    tabs = {"t5": (_rand(rng, 32, 1), None),
+            "shaw": (_rand(rng, 7, d), _rand(rng, 7, d)),
+            "deberta": (_rand(rng, 8, 1, d), _rand(rng, 8, 1, d))}
+    for kind, (t1, t2) in tabs.items():
+        kw = dict(clip_k=3 if kind == "shaw" else 4, q_pos_offset=q_off, causal=True,
+                  n_valid=n_valid, bidirectional=False)
+        a = oracle.relattn_forward_head(q, k, v, kind, 0, t1, t2, **kw)
+        b = oracle.relattn_forward_head(q, k2, v2, kind, 0, t1, t2, **kw)
+        assert np.array_equal(a, b), kind
+        # also: future keys (positions > query) under causal
+        k3, v3 = k.copy(), v.copy()
+        k3[q_off + Lq:] = 55.0
+        v3[q_off + Lq:] = 55.0
+        c = oracle.relattn_forward_head(q, k3, v3, kind, 0, t1, t2, **kw)
+        assert np.array_equal(a, c), kind
+
+
+def test_fully_masked_rows_are_zero():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand(rng, 4, 8), _rand(rng, 6, 8), _rand(rng, 6, 8)
+    got = oracle.relattn_forward_head(q, k, v, "t5", 0, _rand(rng, 32, 1), n_valid=0)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_position_shift_leaves_output_unchanged():
+    # [RPE] "Choosing a scheme": shifting the input by a constant leaves the
+    # attention pattern unchanged.
+    rng = np.random.default_rng(9)
+    q, k, v = _rand(rng, 10, 8), _rand(rng, 14, 8), _rand(rng, 14, 8)
+    cases = {"t5": (_rand(rng, 32, 1), None, {}),
+             "shaw": (_rand(rng, 9, 8), _rand(rng, 9, 8), dict(clip_k=4)),
+             "deberta": (_rand(rng, 10, 1, 8), _rand(rng, 10, 1, 8), dict(clip_k=5))}
+    for kind, (t1, t2, kw) in cases.items():
+        a = oracle.relattn_forward_head(q, k, v, kind, 0, t1, t2, q_pos_offset=3, **kw)
+        b = oracle.relattn_forward_head(q, k, v, kind, 0, t1, t2, q_pos_offset=903,
+                                        k_pos_offset=900, **kw)
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_rows_selection_matches_full():
+    rng = np.random.default_rng(10)
+    q, k, v = _rand(rng, 2, 3, 21, 8), _rand(rng, 2, 3, 21, 8), _rand(rng, 2, 3, 21, 8)
+    kr, qr = _rand(rng, 8, 3, 8), _rand(rng, 8, 3, 8)
+    full = oracle.relattn_forward(q, k, v, "deberta", kr, qr, clip_k=4, causal=True)
+    part = oracle.relattn_forward(q, k, v, "deberta", kr, qr, clip_k=4, causal=True,
+                                  heads=[(1, 2), (0, 1)], rows=[0, 5, 20])
+    np.testing.assert_allclose(part[0], full[1, 2, [0, 5, 20]], atol=1e-13)
+    np.testing.assert_allclose(part[1], full[0, 1, [0, 5, 20]], atol=1e-13)
+
+
+# -------------------------------------------------------------- brute force
+
+@settings(max_examples=60, deadline=None)
+@given(kind=st.sampled_from(["t5", "shaw", "deberta"]),
+       Lq=st.integers(1, 9), Lk=st.integers(1, 12), d=st.sampled_from([2, 4, 8]),
+       q_off=st.integers(0, 40), k_off=st.integers(0, 40), causal=st.booleans(),
+       bidir=st.booleans(), nb=st.sampled_from([4, 8, 16, 32, 64]),
+       md=st.sampled_from([8, 20, 128]), clip=st.integers(1, 6),
+       n_valid=st.one_of(st.none(), st.integers(0, 12)), seed=st.integers(0, 10_000))
+def test_vectorised_equals_bruteforce(kind, Lq, Lk, d, q_off, k_off, causal, bidir, nb,
+                                      md, clip, n_valid, seed):
+    slots = nb // 2 if bidir else nb
+    if kind == "t5" and md <= slots // 2:
+        md = slots
+    rng = np.random.default_rng(seed)
+    H, h = 2, seed % 2
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    if kind == "t5":
+        t1, t2 = _rand(rng, nb, H), None
+    elif kind == "shaw":
+        t1, t2 = _rand(rng, 2 * clip + 1, d), _rand(rng, 2 * clip + 1, d)
+    else:
+        t1, t2 = _rand(rng, 2 * clip, H, d), _rand(rng, 2 * clip, H, d)
+    kw = dict(num_buckets=nb, max_distance=md, bidirectional=bidir, clip_k=clip,
+              q_pos_offset=q_off, k_pos_offset=k_off, causal=causal, n_valid=n_valid)
+    a = oracle.relattn_forward_head(q, k, v, kind, h, t1, t2, **kw)
+    b = oracle.relattn_forward_bruteforce(q, k, v, kind, h, t1, t2, **kw)
+    np.testing.assert_allclose(a, b, atol=1e-11, rtol=0)
