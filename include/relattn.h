@@ -1,0 +1,164 @@
+/*
+ * relattn.h -- C ABI of the fused relative-position attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (page title, then the passage):
+ *   [RPE]  "Relative Position Embeddings, in depth: Shaw, Transformer-XL,
+ *          T5 buckets and DeBERTa ..." (aicassindra.com)
+ *   [T5B]  "T5 Relative-Position Bias" (liminalml.com)
+ *   [DRPE] "DeBERTa > Relative Position Encoding" (mbrenndoerfer.com)
+ *
+ * One call computes, for every (batch b, head h, query row i):
+ *
+ *   out[b,h,i,:] = sum_j softmax_j(s_ij) * value_ij
+ *
+ * over the keys j that are visible to row i, where, with absolute query
+ * position p_i = q_pos_offset + i and key position j,
+ *
+ *   T5      s_ij = scale * q_i.k_j + table[bucket(j - p_i), h]
+ *           value_ij = v_j
+ *           bucket(): [RPE] "T5: one scalar per head, looked up by bucket"
+ *           and [T5B] (offset = key - query; bidirectional splits the
+ *           buckets by direction; causal bucketing clamps forward offsets
+ *           to distance 0).  The bias is added after scaling.
+ *   SHAW    s_ij = scale * q_i.(k_j + a_K[r_ij]),  r_ij = clip(j - p_i, -k, k) + k
+ *           value_ij = v_j + a_V[r_ij]
+ *           [RPE] "Shaw et al.: learned vectors on keys and values".
+ *   DEBERTA s_ij = scale * (q_i.k_j + q_i.Kr[d(p_i, j), h] + k_j.Qr[d(j, p_i), h])
+ *           d(x, y) = clip(x - y, -k, k - 1) + k, value_ij = v_j
+ *           [DRPE] "The Relative Position Formula" (clip-and-shift index,
+ *           2k rows); [RPE] "DeBERTa: disentangled content and position"
+ *           (content-to-position plus position-to-content, scale 1/sqrt(3d)).
+ *
+ * Offset conventions (documented because mixing them swaps past and future,
+ * [RPE] "Failure modes"): T5 and Shaw index by key - query; DeBERTa's
+ * d(i, j) takes query - key.
+ *
+ * Visibility: key j is hidden when causal != 0 and j > p_i, and when
+ * kv_valid_len != NULL and j >= kv_valid_len[b].  Masking is independent of
+ * bucketing ([T5B]): a forward offset that maps to bucket 0 is still hidden
+ * under the causal mask.  A row with no visible key produces zeros.
+ *
+ * Neither the L x L bias nor any L x L x d tensor is written to memory: the
+ * relative term is formed inside the tile loop ([RPE] "Kernels and the KV
+ * cache: where the choice bites").
+ *
+ * Conventions for every entry point
+ *   - Ownership: the caller owns all buffers.  The library allocates no
+ *     device memory and keeps no state between calls; calls are re-entrant.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream) and the call returns without waiting.
+ *   - Validation: every argument is checked on the host before anything is
+ *     enqueued; on failure nothing is launched and a status is returned.
+ *     relattn_last_error() then describes the failure (thread-local).
+ *   - Launch failures reported by the HIP runtime return RELATTN_ERR_HIP.
+ */
+#ifndef RELATTN_H
+#define RELATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RELATTN_ABI_VERSION 1
+
+typedef enum {
+    RELATTN_T5 = 0,
+    RELATTN_SHAW = 1,
+    RELATTN_DEBERTA = 2
+} relattn_kind;
+
+typedef enum {
+    RELATTN_FP32 = 0,   /* float32 inputs, float32 arithmetic, float32 output   */
+    RELATTN_BF16 = 1    /* bfloat16 inputs, float32 accumulation, bf16 output     */
+} relattn_dtype;
+
+typedef enum {
+    RELATTN_OK = 0,
+    RELATTN_ERR_INVALID = 1,      /* malformed argument (null pointer, bad size) */
+    RELATTN_ERR_UNSUPPORTED = 2,  /* well-formed but outside what is built      */
+    RELATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than needed   */
+    RELATTN_ERR_HIP = 4           /* the HIP runtime reported an error          */
+} relattn_status;
+
+/*
+ * Problem description.  Tensor layouts (all row-major and contiguous):
+ *   q, out : [B, H, Lq, d]      k, v : [B, H, Lk, d]      element type = dtype
+ *   T5      table  : float32 [num_buckets, H]       table2 : unused (NULL)
+ *   SHAW    table  : a_K [2*clip_k + 1, d] (dtype)  table2 : a_V, same shape;
+ *           shared by all heads ([RPE] Shaw section)
+ *   DEBERTA table  : Kr [2*clip_k, H, d] (dtype)    table2 : Qr, same shape
+ * Device pointers must be 16-byte aligned.
+ */
+typedef struct {
+    int32_t kind;            /* relattn_kind                                     */
+    int32_t dtype;           /* relattn_dtype                                    */
+    int32_t B, H, Lq, Lk, d; /* d in {32, 64}                                    */
+    const void *table;       /* device pointer, see above                        */
+    const void *table2;      /* device pointer, see above                        */
+    int32_t num_buckets;     /* T5: total buckets (2..256)                       */
+    int32_t max_distance;    /* T5: distance where log buckets end (> exact range) */
+    int32_t bidirectional;   /* T5: nonzero = split buckets by direction         */
+    int32_t clip_k;          /* SHAW (1..32) / DEBERTA (1..65536): clip k        */
+    int32_t q_pos_offset;    /* absolute position of query row 0 (>= 0); keys
+                                sit at positions 0..Lk-1 ([T5B], cached decoder) */
+    int32_t causal;          /* nonzero: hide keys after the query's position    */
+    const int32_t *kv_valid_len; /* device int32 [B] or NULL: keys j >= len hidden */
+    float scale;             /* 0 = default: 1/sqrt(d) (T5, SHAW), 1/sqrt(3d)
+                                (DEBERTA)                                       */
+} relattn_params;
+
+/*
+ * Fused forward.  q, k, v, out: device pointers as described above.
+ * workspace: device buffer of at least relattn_workspace_bytes() bytes
+ * (may be NULL when that size is 0); its contents on entry do not matter and
+ * on return are unspecified.  Two calls that share a workspace must be
+ * ordered on one stream.
+ * Returns RELATTN_OK once all kernels are enqueued.
+ */
+relattn_status relattn_fwd(const relattn_params *p, const void *q, const void *k,
+                           const void *v, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace relattn_fwd needs for this problem (split-KV
+ * partial results and DeBERTa's per-key position constants). */
+relattn_status relattn_workspace_bytes(const relattn_params *p, size_t *bytes);
+
+/*
+ * Relative index of n (query position, key position) pairs, computed by the
+ * same device index functions the fused kernel uses:
+ *   which = 0: T5 bucket(k_pos - q_pos) | SHAW clip(k_pos - q_pos, -k, k) + k |
+ *              DEBERTA d(q_pos, k_pos)
+ *   which = 1: DEBERTA d(k_pos, q_pos) (position-to-content index); other
+ *              kinds reject it.
+ * Only kind and the kind's index parameters of *p are read (shapes and
+ * tables are ignored).  q_pos, k_pos: device int32 [n]; idx_out: device
+ * int32 [n].  n may be 0 (nothing is launched).
+ */
+relattn_status relattn_rel_index(const relattn_params *p, const int32_t *q_pos,
+                                 const int32_t *k_pos, int64_t n, int32_t which,
+                                 int32_t *idx_out, void *stream);
+
+/*
+ * T5 bucket thresholds as the kernels use them (host computation, no GPU):
+ * thr[m] for m = 0 .. slots - exact - 1 is the smallest distance whose
+ * within-direction slot is >= exact + m, evaluated with the pages' float64
+ * logarithm formula.  *count receives slots - exact; at most `cap` entries
+ * are written.
+ */
+relattn_status relattn_t5_thresholds(int32_t num_buckets, int32_t max_distance,
+                                     int32_t bidirectional, int32_t *thr,
+                                     int32_t cap, int32_t *count);
+
+const char *relattn_status_str(relattn_status s);
+const char *relattn_last_error(void);
+int32_t relattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELATTN_H */

@@ -1,0 +1,152 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+declared symbol, validates arguments before any HIP call, and its host-side
+T5 thresholds reproduce the exact-integer bucket criterion."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import transformer_attention_relative_amd as ra
+from transformer_attention_relative_amd.binding import relattn_params
+from tests.closed_forms import t5_bucket_exact
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "relattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ra.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(relattn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_binding_exports():
+    assert set(_declared_functions()) == set(ra.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.relattn_abi_version() == 1
+
+
+def _params(**kw):
+    base = dict(kind="t5", dtype="bf16", B=1, H=2, Lq=64, Lk=64, d=64)
+    base.update(kw)
+    args = [base.pop(k) for k in ("kind", "dtype", "B", "H", "Lq", "Lk", "d")]
+    return ra.make_params(*args, **base)
+
+
+class _FakeTensor:
+    """Stands in for a tensor when only the pointer value is marshalled."""
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+FAKE = _FakeTensor(0x10000)
+
+
+def _fwd_status(lib, p):
+    # q/k/v/out are NULL: even if validation of the params passed, the
+    # pointer checks would stop the call before any launch.
+    return lib.relattn_fwd(ctypes.byref(p), None, None, None, None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kind="t5"), 1),                                   # table NULL
+    (dict(kind="t5", table=FAKE, d=48), 2),                 # unsupported head dim
+    (dict(kind="t5", table=FAKE, d=0), 1),
+    (dict(kind="t5", table=FAKE, B=0), 1),
+    (dict(kind="t5", table=FAKE, Lk=0), 1),
+    (dict(kind="t5", table=FAKE, num_buckets=2), 1),        # no exact slot per half
+    (dict(kind="t5", table=FAKE, num_buckets=1, bidirectional=False), 1),
+    (dict(kind="t5", table=FAKE, max_distance=8), 1),       # max_distance inside exact range
+    (dict(kind="t5", table=FAKE, num_buckets=512), 1),
+    (dict(kind="t5", table=FAKE, num_buckets=32, max_distance=100000), 2),  # LUT too large
+    (dict(kind="t5", table=FAKE, q_pos_offset=-1), 1),
+    (dict(kind="t5", table=FAKE, scale=-1.0), 1),
+    (dict(kind="t5", table=FAKE, scale=float("inf")), 1),
+    (dict(kind="shaw", table=FAKE, clip_k=4), 1),           # table2 NULL
+    (dict(kind="shaw", table=FAKE, table2=FAKE, clip_k=0), 1),
+    (dict(kind="shaw", table=FAKE, table2=FAKE, clip_k=33), 2),
+    (dict(kind="deberta", table=FAKE, table2=FAKE, clip_k=0), 1),
+    (dict(kind="deberta", table=FAKE, table2=_FakeTensor(0x10004), clip_k=4), 1),  # misaligned
+    (dict(kind="t5", table=FAKE), 1),                       # valid params, NULL tensors
+])
+def test_fwd_validation_rejects_before_launch(lib, kw, status):
+    p = _params(**kw)
+    assert _fwd_status(lib, p) == status
+    assert lib.relattn_last_error().decode() != ""
+
+
+def test_fwd_rejects_bad_kind_and_dtype(lib):
+    p = _params(table=FAKE)
+    p.kind = 7
+    assert _fwd_status(lib, p) == 1
+    p = _params(table=FAKE)
+    p.dtype = 5
+    assert _fwd_status(lib, p) == 1
+    assert lib.relattn_fwd(None, None, None, None, None, None, 0, None) == 1
+
+
+def test_fwd_workspace_too_small(lib):
+    # decode-like problem: few workgroups -> split-KV partials in the workspace
+    p = _params(kind="t5", table=FAKE, B=1, H=2, Lq=128, Lk=8192, q_pos_offset=8064,
+                causal=True, bidirectional=False)
+    need = ra.relattn_workspace_bytes(p)
+    assert need > 0
+    st = lib.relattn_fwd(ctypes.byref(p), 0x10000, 0x10000, 0x10000, 0x10000, 0x10000,
+                         need - 1, None)
+    assert st == 3
+    st = lib.relattn_fwd(ctypes.byref(p), 0x10000, 0x10000, 0x10000, 0x10000, None, need, None)
+    assert st == 3
+
+
+def test_workspace_sizes():
+    p = _params(kind="t5", table=FAKE, B=8, H=12, Lq=512, Lk=512)
+    assert ra.relattn_workspace_bytes(p) == 0          # enough workgroups, no split
+    p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=512, B=8, H=12,
+                Lq=2048, Lk=2048)
+    assert ra.relattn_workspace_bytes(p) >= 2 * 96 * 2048 * 4   # per-key constants
+
+
+def test_rel_index_validation(lib):
+    p = _params(kind="shaw", clip_k=0)
+    assert lib.relattn_rel_index(ctypes.byref(p), None, None, 4, 0, None, None) == 1
+    p = _params(kind="t5")
+    assert lib.relattn_rel_index(ctypes.byref(p), None, None, 4, 1, None, None) == 1  # which=1 is DeBERTa only
+    assert lib.relattn_rel_index(ctypes.byref(p), None, None, -1, 0, None, None) == 1
+    assert lib.relattn_rel_index(ctypes.byref(p), None, None, 0, 0, None, None) == 0  # nothing to do
+    assert lib.relattn_rel_index(ctypes.byref(p), None, None, 3, 0, None, None) == 1  # NULL buffers
+
+
+@pytest.mark.parametrize("nb,md", [(8, 16), (16, 64), (32, 128), (32, 256), (64, 128),
+                                   (64, 512), (128, 1024), (32, 4096), (30, 100), (256, 4096)])
+@pytest.mark.parametrize("bidir", [True, False])
+def test_host_thresholds_match_exact_criterion(nb, md, bidir):
+    """Buckets rebuilt from the library's thresholds equal the exact-integer
+    closed form for every offset in [-8192, 8192] (bit-exact integer work)."""
+    thr = ra.relattn_t5_thresholds(nb, md, bidir)
+    slots = nb // 2 if bidir else nb
+    exact = slots // 2
+    assert len(thr) == slots - exact and thr[0] == exact
+    assert all(a <= b for a, b in zip(thr, thr[1:]))
+    thr_arr = np.array(thr[1:], dtype=np.int64)
+    for off in range(-8192, 8193, 1 if nb <= 64 else 7):
+        if bidir:
+            base, dist = (slots if off > 0 else 0), abs(off)
+        else:
+            base, dist = 0, max(-off, 0)
+        got = base + (dist if dist < exact else exact + int((dist >= thr_arr).sum()))
+        assert got == t5_bucket_exact(off, bidir, nb, md), (off, got)

@@ -1,0 +1,296 @@
+"""HIP path against the float64 oracle, through the C ABI, on the GPU.
+
+Bars: indices bit-exact; float32 outputs within 1e-5 max-abs; bfloat16
+outputs within 2e-2 max-abs and 2e-3 mean-abs of the oracle (fp32
+accumulation inside the kernels).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_relative_amd as ra
+from transformer_attention_relative_amd.synthetic import WORKLOADS, Workload, make_inputs, params_of
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+TOL = {"fp32": (1e-5, 1e-5), "bf16": (2e-2, 2e-3)}
+
+
+def _np(t):
+    return None if t is None else t.float().numpy().astype(np.float64)
+
+
+def _to_dev(inp):
+    return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+
+
+def run_gpu(wl: Workload, dev_inp):
+    out = ra.relattn_fwd(dev_inp["q"], dev_inp["k"], dev_inp["v"], wl.kind, dev_inp["table"],
+                         dev_inp["table2"], kv_valid_len=dev_inp["kv_valid_len"], **params_of(wl))
+    torch.cuda.synchronize()
+    return out
+
+
+def run_oracle(wl: Workload, inp, heads=None, rows=None):
+    return oracle.relattn_forward(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), wl.kind,
+                                  _np(inp["table"]), _np(inp["table2"]),
+                                  kv_valid_len=None if inp["kv_valid_len"] is None
+                                  else inp["kv_valid_len"].numpy(),
+                                  heads=heads, rows=rows, **params_of(wl))
+
+
+def check_close(got, want, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    max_tol, mean_tol = TOL[dtype]
+    assert err.max() <= max_tol, f"{what}: max-abs {err.max():.3e} > {max_tol}"
+    assert err.mean() <= mean_tol, f"{what}: mean-abs {err.mean():.3e} > {mean_tol}"
+    return err.max(), err.mean()
+
+
+# ----------------------------------------------------------------------------
+# 1. indices, bit-exact, over every (query, key) pair of every workload
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_rel_index_bit_exact_full_grid(name):
+    wl = WORKLOADS[name]
+    qpos = wl.q_pos_offset + np.arange(wl.Lq)
+    kpos = np.arange(wl.Lk)
+    QP, KP = np.meshgrid(qpos, kpos, indexing="ij")
+    qp = torch.from_numpy(QP.reshape(-1).astype(np.int32)).to(DEV)
+    kp = torch.from_numpy(KP.reshape(-1).astype(np.int32)).to(DEV)
+    kw = dict(num_buckets=wl.num_buckets, max_distance=wl.max_distance,
+              bidirectional=wl.bidirectional, clip_k=wl.clip_k)
+    want = oracle.rel_index_matrices(wl.kind, wl.Lq, wl.Lk, q_pos_offset=wl.q_pos_offset, **kw)
+    got = ra.relattn_rel_index(wl.kind, qp, kp, 0, **kw).cpu().numpy().reshape(wl.Lq, wl.Lk)
+    assert np.array_equal(got, want["idx"])
+    if wl.kind == "deberta":
+        got2 = ra.relattn_rel_index(wl.kind, qp, kp, 1, **kw).cpu().numpy().reshape(wl.Lq, wl.Lk)
+        assert np.array_equal(got2, want["idx2"])
+
+
+@pytest.mark.parametrize("nb,md", [(32, 128), (64, 128), (16, 40), (32, 1000), (256, 4096), (30, 100)])
+@pytest.mark.parametrize("bidir", [True, False])
+def test_t5_bucket_bit_exact_wide_offsets(nb, md, bidir):
+    offs = np.arange(-20000, 20001)
+    qp = torch.full((offs.size,), 20000, dtype=torch.int32, device=DEV)
+    kp = torch.from_numpy((20000 + offs).astype(np.int32)).to(DEV)
+    got = ra.relattn_rel_index("t5", qp, kp, 0, num_buckets=nb, max_distance=md,
+                               bidirectional=bidir).cpu().numpy()
+    want = oracle.t5_bucket_array(offs, bidir, nb, md)
+    assert np.array_equal(got, want)
+
+
+def test_index_page_values_on_gpu():
+    # [T5B]: -17 -> 10 / 26 (bidirectional), 16 / 0 (causal); cached query 128
+    # vs key 124 -> causal 4.  [DRPE]: -k -> 0, 0 -> k, k-1 -> 2k-1.
+    q = torch.tensor([17, 0, 17, 0, 128], dtype=torch.int32, device=DEV)
+    k = torch.tensor([0, 17, 0, 17, 124], dtype=torch.int32, device=DEV)
+    assert ra.relattn_rel_index("t5", q[:2], k[:2], bidirectional=True).tolist() == [10, 26]
+    assert ra.relattn_rel_index("t5", q, k, bidirectional=False).tolist() == [16, 0, 16, 0, 4]
+    kk = 512
+    q = torch.tensor([0, 5, 520], dtype=torch.int32, device=DEV)
+    k = torch.tensor([kk, 5, 9], dtype=torch.int32, device=DEV)   # i - j = -k, 0, k - 1
+    assert ra.relattn_rel_index("deberta", q, k, 0, clip_k=kk).tolist() == [0, kk, 2 * kk - 1]
+
+
+# ----------------------------------------------------------------------------
+# 2. parity at sizes the oracle finishes quickly (several tiles + ragged tails)
+# ----------------------------------------------------------------------------
+
+def _small(kind, dtype, d, **kw):
+    base = dict(name="small", kind=kind, B=2, H=3, Lq=300, Lk=333, d=d, dtype=dtype,
+                table_sigma=0.5 if kind == "t5" else 0.1)
+    base.update(kw)
+    return Workload(**base)
+
+
+SMALL_CASES = []
+for dtype in ("fp32", "bf16"):
+    for d in (32, 64):
+        SMALL_CASES += [
+            _small("t5", dtype, d),
+            _small("t5", dtype, d, bidirectional=False, causal=True, Lq=200, Lk=333, q_pos_offset=133),
+            _small("t5", dtype, d, num_buckets=64, max_distance=100, valid_len_range=(1, 333)),
+            _small("t5", dtype, d, num_buckets=16, max_distance=40, causal=True, Lq=333),
+            _small("shaw", dtype, d, clip_k=16, causal=True, Lq=333),
+            _small("shaw", dtype, d, clip_k=5, causal=False, valid_len_range=(100, 333)),
+            _small("shaw", dtype, d, clip_k=1, causal=True, Lq=150, q_pos_offset=183),
+            _small("shaw", dtype, d, clip_k=32, causal=False),
+            _small("deberta", dtype, d, clip_k=512),
+            _small("deberta", dtype, d, clip_k=16, valid_len_range=(50, 333)),
+            _small("deberta", dtype, d, clip_k=3, causal=True, Lq=333),
+            _small("deberta", dtype, d, clip_k=40, causal=True, Lq=100, q_pos_offset=233),
+        ]
+
+
+def _case_id(wl):
+    s = f"{wl.kind}-{wl.dtype}-d{wl.d}-Lq{wl.Lq}-Lk{wl.Lk}"
+    if wl.kind == "t5":
+        s += f"-nb{wl.num_buckets}-md{wl.max_distance}-{'bi' if wl.bidirectional else 'uni'}"
+    else:
+        s += f"-k{wl.clip_k}"
+    s += "-causal" if wl.causal else ""
+    s += f"-q{wl.q_pos_offset}" if wl.q_pos_offset else ""
+    s += "-pad" if wl.valid_len_range else ""
+    return s
+
+
+@pytest.mark.parametrize("wl", SMALL_CASES, ids=_case_id)
+def test_parity_small(wl):
+    inp = make_inputs(wl, seed=11)
+    got = run_gpu(wl, _to_dev(inp)).cpu()
+    want = run_oracle(wl, inp)
+    check_close(got.float().numpy(), want, wl.dtype, _case_id(wl))
+
+
+DECODE_CASES = [
+    Workload(name="dec", kind="t5", B=1, H=2, Lq=128, Lk=2000, d=64, dtype="bf16",
+             bidirectional=False, causal=True, q_pos_offset=1872),
+    Workload(name="dec", kind="t5", B=1, H=3, Lq=40, Lk=3001, d=32, dtype="fp32",
+             bidirectional=False, causal=True, q_pos_offset=2961),
+    Workload(name="dec", kind="shaw", B=1, H=2, Lq=70, Lk=2500, d=64, dtype="bf16",
+             clip_k=16, causal=True, q_pos_offset=2430, table_sigma=0.1),
+    Workload(name="dec", kind="shaw", B=1, H=1, Lq=33, Lk=2100, d=64, dtype="fp32",
+             clip_k=7, causal=False, table_sigma=0.1),
+    Workload(name="dec", kind="deberta", B=1, H=2, Lq=100, Lk=2300, d=64, dtype="bf16",
+             clip_k=512, causal=False, table_sigma=0.1),
+    Workload(name="dec", kind="deberta", B=2, H=1, Lq=64, Lk=1800, d=32, dtype="fp32",
+             clip_k=100, causal=True, q_pos_offset=1736, table_sigma=0.1),
+]
+
+
+@pytest.mark.parametrize("wl", DECODE_CASES, ids=_case_id)
+def test_parity_split_kv(wl):
+    # few workgroups: the key range is split and the partials are merged
+    p = ra.make_params(wl.kind, wl.dtype, wl.B, wl.H, wl.Lq, wl.Lk, wl.d,
+                       table=torch.empty(16, device=DEV), table2=torch.empty(16, device=DEV),
+                       clip_k=max(wl.clip_k, 1), **{k: v for k, v in params_of(wl).items()
+                                                    if k != "clip_k"})
+    assert ra.relattn_workspace_bytes(p) > 0
+    inp = make_inputs(wl, seed=5)
+    got = run_gpu(wl, _to_dev(inp)).cpu()
+    want = run_oracle(wl, inp)
+    check_close(got.float().numpy(), want, wl.dtype, _case_id(wl))
+
+
+# ----------------------------------------------------------------------------
+# 3. the five workloads at full size, in the benchmark's launch configuration;
+#    the oracle computes sampled (batch, head) pairs and query rows
+# ----------------------------------------------------------------------------
+
+def _sample_rows(Lq, rng):
+    fixed = {0, 1, 31, 32, 63, 64, 127, 128, Lq - 1, Lq - 2}
+    fixed |= set(rng.integers(0, Lq, 24).tolist())
+    return sorted(r for r in fixed if 0 <= r < Lq)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_parity_full_size_sampled(name):
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl, seed=0)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    rng = np.random.default_rng(0)
+    heads = [(0, 0), (wl.B - 1, wl.H - 1), (int(rng.integers(wl.B)), int(rng.integers(wl.H)))]
+    rows = _sample_rows(wl.Lq, rng)
+    want = run_oracle(wl, inp, heads=heads, rows=rows)
+    sel = np.stack([got[b, h][rows] for b, h in heads])
+    check_close(sel, want, wl.dtype, name)
+    assert np.isfinite(got).all()
+
+
+# ----------------------------------------------------------------------------
+# 4. properties: determinism, masking independence, empty rows, readouts
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["t5_encoder_padded", "shaw_causal_k16", "deberta_k512",
+                                  "t5_decoder_kvcache"])
+def test_deterministic(name):
+    wl = WORKLOADS[name]
+    if wl.Lq > 1024:
+        wl = wl.replace(B=1, H=2)
+    dev = _to_dev(make_inputs(wl, seed=1))
+    a = run_gpu(wl, dev).clone()
+    b = run_gpu(wl, dev)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+def test_masked_keys_do_not_matter(kind):
+    # [T5B]: check masking on its own -- perturbing keys that are hidden
+    # (padding, or after the query under the causal mask) leaves the output
+    # bit-identical.
+    wl = _small(kind, "bf16", 64, causal=True, Lq=200, Lk=333, q_pos_offset=100,
+                valid_len_range=(150, 280), clip_k=8 if kind != "t5" else 0,
+                bidirectional=False)
+    inp = make_inputs(wl, seed=3)
+    dev = _to_dev(inp)
+    a = run_gpu(wl, dev).clone()
+    k2, v2 = dev["k"].clone(), dev["v"].clone()
+    lens = inp["kv_valid_len"].tolist()
+    for b, n in enumerate(lens):
+        k2[b, :, n:] = 37.0
+        v2[b, :, n:] = -11.0
+    k2[:, :, 300:] = -5.0        # beyond every query position (100 + 199)
+    v2[:, :, 300:] = 9.0
+    dev2 = dict(dev, k=k2, v=v2)
+    b_ = run_gpu(wl, dev2)
+    assert torch.equal(a, b_)
+
+
+def test_fully_masked_rows_are_zero():
+    wl = _small("t5", "bf16", 64, Lq=130, Lk=200)
+    inp = make_inputs(wl, seed=4)
+    inp["kv_valid_len"] = torch.tensor([0, 50], dtype=torch.int32)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float()
+    assert torch.count_nonzero(got[0]) == 0
+    want = run_oracle(wl, inp)
+    check_close(got.numpy(), want, "bf16")
+
+
+def test_t5_bucket_readout_through_fused_kernel():
+    # Q = K = 0 and table[b, h] = b/4: the scores are the bias alone.  With
+    # V one-hot per key, out[i, j] = softmax_j(bias), so log-ratios give the
+    # bucket differences exactly.
+    for bidir, q_off, causal in ((True, 0, False), (False, 31, True), (True, 100, False)):
+        Lq, Lk, d = 64, 32, 32
+        q = torch.zeros(1, 1, Lq, d, device=DEV)
+        k = torch.zeros(1, 1, Lk, d, device=DEV)
+        v = torch.eye(Lk, d, device=DEV).reshape(1, 1, Lk, d).contiguous()
+        table = (torch.arange(32, dtype=torch.float32) / 4).reshape(32, 1).to(DEV)
+        out = ra.relattn_fwd(q, k, v, "t5", table, bidirectional=bidir, q_pos_offset=q_off,
+                             causal=causal)
+        torch.cuda.synchronize()
+        p = out[0, 0, :, :Lk].double().cpu().numpy()
+        idx = oracle.rel_index_matrices("t5", Lq, Lk, q_pos_offset=q_off, bidirectional=bidir)["idx"]
+        got = np.rint(4 * (np.log(p) - np.log(p[:, :1]))).astype(np.int64)
+        assert np.array_equal(got, idx - idx[:, :1])
+
+
+def test_shaw_bins_readout_through_fused_kernel():
+    # Q = K = V = 0: uniform weights over visible keys, and with a_V = I the
+    # output reads the fraction of visible keys in each clipped-offset bin.
+    for causal, kc, q_off in ((True, 5, 0), (False, 7, 3), (True, 15, 40)):
+        Lq, Lk, d = 96, 80, 32
+        z = torch.zeros(1, 1, Lq, d, device=DEV)
+        zk = torch.zeros(1, 1, Lk, d, device=DEV)
+        a_k = torch.randn(2 * kc + 1, d, device=DEV)
+        a_v = torch.eye(2 * kc + 1, d, device=DEV).contiguous()
+        out = ra.relattn_fwd(z, zk, zk, "shaw", a_k, a_v, clip_k=kc, causal=causal,
+                             q_pos_offset=q_off)
+        torch.cuda.synchronize()
+        got = out[0, 0, :, : 2 * kc + 1].double().cpu().numpy()
+        idx = oracle.rel_index_matrices("shaw", Lq, Lk, q_pos_offset=q_off, clip_k=kc)["idx"]
+        want = np.zeros_like(got)
+        for i in range(Lq):
+            vis = np.arange(Lk) <= q_off + i if causal else np.ones(Lk, bool)
+            if vis.sum():
+                want[i] = np.bincount(idx[i][vis], minlength=2 * kc + 1) / vis.sum()
+        np.testing.assert_allclose(got, want, atol=1e-6)

@@ -1,0 +1,194 @@
+"""Thin ctypes binding over ``librelattn.so`` (declared in include/relattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+from .build import LIB_PATH
+
+KINDS = {"t5": 0, "shaw": 1, "deberta": 2}
+DTYPES = {"fp32": 0, "bf16": 1}
+STATUS = {0: "RELATTN_OK", 1: "RELATTN_ERR_INVALID", 2: "RELATTN_ERR_UNSUPPORTED",
+          3: "RELATTN_ERR_WORKSPACE", 4: "RELATTN_ERR_HIP"}
+
+
+class RelattnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+class relattn_params(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Lq", ctypes.c_int32),
+        ("Lk", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("table", ctypes.c_void_p), ("table2", ctypes.c_void_p),
+        ("num_buckets", ctypes.c_int32), ("max_distance", ctypes.c_int32),
+        ("bidirectional", ctypes.c_int32), ("clip_k", ctypes.c_int32),
+        ("q_pos_offset", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("kv_valid_len", ctypes.c_void_p), ("scale", ctypes.c_float),
+    ]
+
+
+EXPORTS = ("relattn_fwd", "relattn_workspace_bytes", "relattn_rel_index",
+           "relattn_t5_thresholds", "relattn_status_str", "relattn_last_error",
+           "relattn_abi_version")
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load (once) the built library; raise if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or os.environ.get("RELATTN_LIB", LIB_PATH)
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} not found: build it with "
+                               "`python -m transformer_attention_relative_amd.build`")
+        lib = ctypes.CDLL(p)
+        P = ctypes.POINTER(relattn_params)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.relattn_fwd.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        lib.relattn_fwd.restype = i32
+        lib.relattn_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+        lib.relattn_workspace_bytes.restype = i32
+        lib.relattn_rel_index.argtypes = [P, vp, vp, i64, i32, vp, vp]
+        lib.relattn_rel_index.restype = i32
+        lib.relattn_t5_thresholds.argtypes = [i32, i32, i32, ctypes.POINTER(i32), i32,
+                                              ctypes.POINTER(i32)]
+        lib.relattn_t5_thresholds.restype = i32
+        lib.relattn_status_str.argtypes = [i32]
+        lib.relattn_status_str.restype = ctypes.c_char_p
+        lib.relattn_last_error.argtypes = []
+        lib.relattn_last_error.restype = ctypes.c_char_p
+        lib.relattn_abi_version.argtypes = []
+        lib.relattn_abi_version.restype = i32
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise RelattnError(status, lib.relattn_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_params(kind: str, dtype: str, B: int, H: int, Lq: int, Lk: int, d: int, *,
+                table=None, table2=None, num_buckets: int = 32, max_distance: int = 128,
+                bidirectional: bool = True, clip_k: int = 0, q_pos_offset: int = 0,
+                causal: bool = False, kv_valid_len=None, scale: float = 0.0) -> relattn_params:
+    return relattn_params(
+        KINDS[kind], DTYPES[dtype], B, H, Lq, Lk, d, _ptr(table), _ptr(table2),
+        num_buckets, max_distance, int(bool(bidirectional)), clip_k, q_pos_offset,
+        int(bool(causal)), _ptr(kv_valid_len), float(scale))
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def relattn_workspace_bytes(params: relattn_params) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.relattn_workspace_bytes(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int = 32,
+                max_distance: int = 128, bidirectional: bool = True, clip_k: int = 0,
+                q_pos_offset: int = 0, causal: bool = False, kv_valid_len=None,
+                scale: float = 0.0, out=None, workspace=None):
+    """Fused forward on the current HIP stream; returns ``out``.
+
+    q [B, H, Lq, d], k/v [B, H, Lk, d] (float32 or bfloat16, contiguous, on
+    the GPU).  Tables: T5 float32 [num_buckets, H]; Shaw a_K / a_V
+    [2k+1, d]; DeBERTa Kr / Qr [2k, H, d] (input dtype).  ``kv_valid_len``:
+    int32 [B] on the GPU or None.  ``out`` and ``workspace`` are allocated
+    with torch when not given.
+    """
+    import torch
+    lib = load_library()
+    if q.dtype == torch.float32:
+        dtype = "fp32"
+    elif q.dtype == torch.bfloat16:
+        dtype = "bf16"
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("table", table), ("table2", table2),
+                    ("kv_valid_len", kv_valid_len)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if kv_valid_len is not None and kv_valid_len.dtype != torch.int32:
+        raise TypeError("kv_valid_len must be int32")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
+        raise ValueError("k and v must be [B, H, Lk, d] matching q")
+    p = make_params(kind, dtype, B, H, Lq, Lk, d, table=table, table2=table2,
+                    num_buckets=num_buckets, max_distance=max_distance,
+                    bidirectional=bidirectional, clip_k=clip_k, q_pos_offset=q_pos_offset,
+                    causal=causal, kv_valid_len=kv_valid_len, scale=scale)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = relattn_workspace_bytes(p)
+    if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if nbytes else None
+    ws_len = workspace.numel() * workspace.element_size() if (nbytes and workspace is not None) else 0
+    _check(lib, lib.relattn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), ws_ptr, ws_len, _stream_handle(q.device)))
+    return out
+
+
+def relattn_rel_index(kind: str, q_pos, k_pos, which: int = 0, *, num_buckets: int = 32,
+                      max_distance: int = 128, bidirectional: bool = True, clip_k: int = 0,
+                      out=None):
+    """Index of each (q_pos[e], k_pos[e]) pair (int32 GPU tensors) on the GPU."""
+    import torch
+    lib = load_library()
+    if q_pos.shape != k_pos.shape or q_pos.dtype != torch.int32 or k_pos.dtype != torch.int32:
+        raise ValueError("q_pos and k_pos must be int32 tensors of one shape")
+    if out is None:
+        out = torch.empty_like(q_pos)
+    p = make_params(kind, "fp32", 1, 1, 1, 1, 32, num_buckets=num_buckets,
+                    max_distance=max_distance, bidirectional=bidirectional, clip_k=clip_k)
+    _check(lib, lib.relattn_rel_index(ctypes.byref(p), q_pos.data_ptr(), k_pos.data_ptr(),
+                                      q_pos.numel(), which, out.data_ptr(),
+                                      _stream_handle(q_pos.device)))
+    return out
+
+
+def relattn_t5_thresholds(num_buckets: int = 32, max_distance: int = 128,
+                          bidirectional: bool = True) -> list:
+    """Host-computed T5 slot thresholds (see include/relattn.h)."""
+    lib = load_library()
+    buf = (ctypes.c_int32 * 256)()
+    cnt = ctypes.c_int32(0)
+    _check(lib, lib.relattn_t5_thresholds(num_buckets, max_distance, int(bool(bidirectional)),
+                                          buf, 256, ctypes.byref(cnt)))
+    return list(buf[: cnt.value])
+
+
+def default_scale(kind: str, d: int) -> float:
+    return 1.0 / math.sqrt(3 * d) if kind == "deberta" else 1.0 / math.sqrt(d)

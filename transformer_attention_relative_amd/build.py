@@ -1,0 +1,64 @@
+"""Build the gfx950 shared library ``librelattn.so`` in-tree with hipcc.
+
+    python -m transformer_attention_relative_amd.build [-v]
+
+Every call recompiles (a stale library is never reused silently).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_NAME = "librelattn.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+SOURCES = ["relattn_kernels.hip", "relattn_api.cpp"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # packed fp32 instructions stay off for all device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc_path() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build librelattn.so)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source of the library for gfx950; return the .so path."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc_path(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    t0 = time.time()
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout + proc.stderr)
+        raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd)}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        noisy = [l for l in (proc.stdout + proc.stderr).splitlines()
+                 if "packed-fp32-ops" not in l]
+        if noisy:
+            print("\n".join(noisy))
+        print(f"built {LIB_PATH} in {time.time() - t0:.1f}s")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
