@@ -9,11 +9,13 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/relattn.h"
+#include "relattn.h"
 #include "relattn_internal.hpp"
 
 namespace relattn {
-hipError_t launch_fwd(int kind, bool bf, int d, const FwdArgs& a, int grid, int lds, hipStream_t st);
+hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int grid, int lds,
+                      hipStream_t st);
+bool fwd_variant_built(int kind, bool bf, Variant v);
 hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st);
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st);
 hipError_t launch_index(const IndexArgs& a, hipStream_t st);
@@ -61,7 +63,7 @@ struct T5Plan {
   int thr[kT5MaxThr];
 };
 
-relattn_status t5_plan(int num_buckets, int max_distance, int bidirectional, T5Plan* P) {
+relattn_status t5_plan(int num_buckets, int max_distance, int bidirectional, int wave_rows, T5Plan* P) {
   if (num_buckets < 2 || num_buckets > 256)
     return fail(RELATTN_ERR_INVALID, "T5 num_buckets=%d outside [2, 256]", num_buckets);
   const int slots = bidirectional ? num_buckets / 2 : num_buckets;
@@ -90,7 +92,7 @@ relattn_status t5_plan(int num_buckets, int max_distance, int bidirectional, T5P
   }
   P->lsat = P->thr[P->nthr - 1];
   P->rsat = bidirectional ? P->lsat : 0;
-  const int W = kWaveRows + kBK - 1;  // offsets spanned by one wave's tile
+  const int W = wave_rows + kBK - 1;  // offsets spanned by one wave's tile
   P->lut_lo = -P->lsat - W;
   P->lut_n = P->lsat + P->rsat + 2 * W + 1;
   return RELATTN_OK;
@@ -99,6 +101,7 @@ relattn_status t5_plan(int num_buckets, int max_distance, int bidirectional, T5P
 struct Plan {
   bool bf;
   float scale;
+  Variant var;
   int n_qtiles, n_splits, grid, lds, Lk_pad;
   size_t off_part_o, off_part_ml, off_colc, ws_bytes;
   T5Plan t5;
@@ -125,13 +128,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   if (!(p->scale >= 0.f) || std::isinf(p->scale))
     return fail(RELATTN_ERR_INVALID, "scale must be finite and >= 0 (0 = default)");
   if (!p->table) return fail(RELATTN_ERR_INVALID, "table is NULL");
-  if (p->kind == RELATTN_T5) {
-    relattn_status s = t5_plan(p->num_buckets, p->max_distance, p->bidirectional, &P->t5);
-    if (s != RELATTN_OK) return s;
-    if (P->t5.lut_n > kT5MaxLut)
-      return fail(RELATTN_ERR_UNSUPPORTED, "T5 saturation distance %d too large for the LDS table",
-                  P->t5.lsat);
-  } else {
+  if (p->kind != RELATTN_T5) {
     if (!p->table2) return fail(RELATTN_ERR_INVALID, "table2 is NULL");
     if (!aligned16(p->table) || !aligned16(p->table2))
       return fail(RELATTN_ERR_INVALID, "tables must be 16-byte aligned");
@@ -145,8 +142,41 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   const float dflt = p->kind == RELATTN_DEBERTA ? 1.f / std::sqrt(3.f * p->d) : 1.f / std::sqrt((float)p->d);
   P->scale = p->scale > 0.f ? p->scale : dflt;
 
+  // Kernel variant.  DeBERTa: 8 waves x 32 rows in bfloat16 (its near-block
+  // bands need 13 KiB of LDS per wave), 4 waves in float32.  T5 / Shaw: 4 waves; 64 rows per wave when there
+  // are enough workgroups to fill two per CU (one LDS fragment then feeds two
+  // MFMAs) and the LDS fits two workgroups per CU, else 32 rows per wave.
+  // float32 always uses 32 rows per wave (its fragments are twice as large).
   const int BH = p->B * p->H;
-  P->n_qtiles = (p->Lq + kBQ - 1) / kBQ;
+  auto lds_for = [&](Variant v, int* total, int* lut_n) -> relattn_status {
+    *lut_n = 0;
+    if (p->kind == RELATTN_T5) {
+      relattn_status s = t5_plan(p->num_buckets, p->max_distance, p->bidirectional,
+                                 kBlockRows * v.qb, &P->t5);
+      if (s != RELATTN_OK) return s;
+      if (P->t5.lut_n > kT5MaxLut)
+        return fail(RELATTN_ERR_UNSUPPORTED, "T5 saturation distance %d too large for the LDS table",
+                    P->t5.lsat);
+      *lut_n = P->t5.lut_n;
+    }
+    *total = lds_layout(p->kind, P->bf, p->d, v.qb, v.nw, p->clip_k, *lut_n).total;
+    return RELATTN_OK;
+  };
+  Variant var = (p->kind == RELATTN_DEBERTA && P->bf) ? Variant{8, 1} : Variant{4, 1};
+  int lds_total = 0, lut_n = 0;
+  if (p->kind != RELATTN_DEBERTA && P->bf) {
+    const int64_t wgs2 = (int64_t)BH * ((p->Lq + 4 * 64 - 1) / (4 * 64));
+    int t2 = 0;
+    if (wgs2 >= 2 * kNumCU && lds_for(Variant{4, 2}, &t2, &lut_n) == RELATTN_OK &&
+        t2 <= kLdsPerCU / 2)
+      var = Variant{4, 2};
+  }
+  relattn_status ls = lds_for(var, &lds_total, &lut_n);
+  if (ls != RELATTN_OK) return ls;
+  if (!fwd_variant_built(p->kind, P->bf, var)) return fail(RELATTN_ERR_UNSUPPORTED, "no kernel variant");
+  P->var = var;
+  const int BQ = kBlockRows * var.qb * var.nw;
+  P->n_qtiles = (p->Lq + BQ - 1) / BQ;
   const int64_t wgs = (int64_t)BH * P->n_qtiles;
   const int64_t kv_reach = p->causal ? std::min<int64_t>(p->Lk, (int64_t)p->q_pos_offset + p->Lq) : p->Lk;
   const int64_t kt = (kv_reach + kBK - 1) / kBK;
@@ -163,9 +193,8 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   const int64_t grid = wgs * splits;
   if (grid > 0x7fffffff) return fail(RELATTN_ERR_UNSUPPORTED, "grid too large");
   P->grid = (int)grid;
-  const LdsLayout L = lds_layout(p->kind, P->bf, p->d, p->clip_k, p->kind == 0 ? P->t5.lut_n : 0);
-  if (L.total > 160 * 1024) return fail(RELATTN_ERR_UNSUPPORTED, "LDS need %d B above 160 KiB", L.total);
-  P->lds = L.total;
+  if (lds_total > kLdsPerCU) return fail(RELATTN_ERR_UNSUPPORTED, "LDS need %d B above 160 KiB", lds_total);
+  P->lds = lds_total;
   P->Lk_pad = (p->Lk + kBK - 1) / kBK * kBK;
 
   size_t off = 0;
@@ -206,7 +235,7 @@ const char* relattn_last_error(void) { return g_last_error.c_str(); }
 relattn_status relattn_t5_thresholds(int32_t num_buckets, int32_t max_distance, int32_t bidirectional,
                                      int32_t* thr, int32_t cap, int32_t* count) {
   T5Plan P;
-  relattn_status s = t5_plan(num_buckets, max_distance, bidirectional, &P);
+  relattn_status s = t5_plan(num_buckets, max_distance, bidirectional, kBlockRows, &P);
   if (s != RELATTN_OK) return s;
   if (count) *count = P.nthr;
   if (thr)
@@ -269,7 +298,7 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
     e = launch_colc(P.bf, p->d, ca, st);
     if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "colc launch: %s", hipGetErrorString(e));
   }
-  e = launch_fwd(p->kind, P.bf, p->d, a, P.grid, P.lds, st);
+  e = launch_fwd(p->kind, P.bf, p->d, P.var, a, P.grid, P.lds, st);
   if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   if (P.n_splits > 1) {
     CombineArgs cb{a.part_o, a.part_ml, out, p->B * p->H, p->Lq, P.n_splits};
@@ -291,7 +320,7 @@ relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, 
   std::memset(&a, 0, sizeof a);
   if (p->kind == RELATTN_T5) {
     T5Plan P;
-    relattn_status s = t5_plan(p->num_buckets, p->max_distance, p->bidirectional, &P);
+    relattn_status s = t5_plan(p->num_buckets, p->max_distance, p->bidirectional, kBlockRows, &P);
     if (s != RELATTN_OK) return s;
     a.t5_slots = P.slots; a.t5_exact = P.exact; a.t5_bidir = p->bidirectional ? 1 : 0;
     a.t5_nthr = P.nthr;

@@ -14,20 +14,17 @@
 namespace relattn {
 
 // ---- work decomposition -------------------------------------------------
-// One workgroup = 4 wave64s; each wave owns 32 consecutive query rows, so a
-// workgroup covers a 128-row query tile of one (batch, head).  Keys are
-// streamed in tiles of kBK rows through LDS.
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveRows = 32;
-constexpr int kBQ = kWaveRows * kWaves;  // 128 query rows per workgroup
-constexpr int kBK = 64;                  // keys per tile
+// A workgroup is NW wave64s; each wave owns QB blocks of 32 consecutive query
+// rows of one (batch, head).  Keys stream through LDS in tiles of kBK rows.
+constexpr int kBK = 64;        // keys per tile
+constexpr int kBlockRows = 32; // query rows per MFMA block
 
 // ---- limits checked by the host before launch -----------------------------
 constexpr int kT5MaxThr = 128;   // slots - exact <= 128  (num_buckets <= 256)
 constexpr int kT5MaxLut = 4096;  // entries of the per-head offset -> bias table
 constexpr int kShawMaxK = 32;
 constexpr int kMaxSplits = 32;
+constexpr int kLdsPerCU = 160 * 1024;
 
 // Kernel argument block (passed by value).
 struct FwdArgs {
@@ -72,47 +69,66 @@ struct ColcArgs {
   int32_t BH, H, Lk, Lk_pad, clip_k;
 };
 
-// ---- LDS layout ------------------------------------------------------------
-// K tile:  bf16 [kBK][d + 8]  (row stride keeps 16-byte rows, staggers banks)
-//          fp32 [kBK][d + 4]
-// V tile:  bf16 transposed [d][kBK + 4] (the PV product contracts over keys,
-//          so each lane reads 4-key runs of one head-dim row)
-//          fp32 row-major [kBK][d + 4]
-// Both double-buffered.  After them, per kind:
-//   T5      float lut[lut_n]
-//   SHAW    per wave: float arel[32][2k+1], float slog[32][2k-1]
-//   DEBERTA per wave: float cband[32][kBK + 36], float pband[32][kBK + 4]
-struct LdsLayout {
-  int k_off, v_off, rel_off, total;
-  int k_stride, v_stride;       // elements
-  int wave_rel_floats;          // per-wave floats of the kind region
-  int arel_stride, slog_stride; // SHAW
-  int cband_stride, pband_stride; // DEBERTA
+// Kernel variant: waves per workgroup and 32-row query blocks per wave.
+struct Variant {
+  int nw, qb;
 };
 
-RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int clip_k, int lut_n) {
+// Key/value stages in flight (global -> LDS ring depth) per kind.
+RELATTN_HD constexpr int num_stages(int kind, bool bf16) { return kind == 0 ? (bf16 ? 4 : 3) : 2; }
+
+// Shaw bins strictly inside the clip window (offsets -k+1 .. k-1), padded to
+// whole MFMA contraction chunks.
+RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k - 1) + 15) / 16 * 16; }
+
+// ---- LDS layout ------------------------------------------------------------
+// Stage s holds the K tile then the V tile of one key tile, each kBK rows of
+// d elements, row-major; 16-byte chunks are XOR-swizzled within a row
+// (chunk c of row r sits in slot c ^ (r & 7)) so that column reads of
+// consecutive rows hit different banks.  After the stages, per kind:
+//   T5      float lut4[4][lut_stride]: four copies of bias[offset]/scale,
+//           copy c shifted by c entries, so any 4 consecutive offsets are one
+//           aligned 16-byte read
+//   SHAW    per wave: float arel[rows][2k+1]; per wave: bin scratch
+//           [32][bin_slots] (input dtype); bf16 only: a_V^T [d][bin_slots]
+//   DEBERTA per wave: float cband[32][kCbandStride], float pband[32][kPbandStride]
+constexpr int kCbandStride = 68;  // 63 band rows, padded so that rows hit distinct banks
+constexpr int kPbandStride = 36;  // 32 keys, padded; rows stay 16-byte aligned
+
+struct LdsLayout {
+  int stage_bytes, tile_bytes, rel_off, total;
+  int lut_stride;
+  int arel_stride, arel_wave_floats, wscr_off, wscr_wave_bytes, avt_off;
+  int deb_wave_floats;
+};
+
+RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int nw, int clip_k,
+                                       int lut_n) {
   LdsLayout L{};
   const int esz = bf16 ? 2 : 4;
-  L.k_stride = bf16 ? d + 8 : d + 4;
-  L.v_stride = bf16 ? kBK + 4 : d + 4;
-  const int k_bytes = 2 * kBK * L.k_stride * esz;
-  const int v_bytes = bf16 ? 2 * d * L.v_stride * esz : 2 * kBK * L.v_stride * esz;
-  L.k_off = 0;
-  L.v_off = k_bytes;
-  L.rel_off = (k_bytes + v_bytes + 15) & ~15;
+  L.tile_bytes = kBK * d * esz;
+  L.stage_bytes = 2 * L.tile_bytes;
+  L.rel_off = num_stages(kind, bf16) * L.stage_bytes;
   int rel_bytes = 0;
   if (kind == 0) {
-    rel_bytes = lut_n * 4;
+    // stride = 16 (mod 64) floats: four lanes reading the four copies at one
+    // aligned position land in different bank groups
+    L.lut_stride = ((lut_n + 3) + 63 - 16) / 64 * 64 + 16;
+    rel_bytes = 4 * L.lut_stride * 4;
   } else if (kind == 1) {
-    L.arel_stride = 2 * clip_k + 1;
-    L.slog_stride = 2 * clip_k - 1 > 0 ? 2 * clip_k - 1 : 1;
-    L.wave_rel_floats = kWaveRows * (L.arel_stride + L.slog_stride);
-    rel_bytes = kWaves * L.wave_rel_floats * 4;
+    const int rows = kBlockRows * qb;
+    const int nbin = shaw_bin_slots(clip_k);
+    // even stride: a row read at offset (const - row) walks 33 banks per row
+    L.arel_stride = 2 * clip_k + 2;
+    L.arel_wave_floats = rows * L.arel_stride;
+    const int arel_bytes = (nw * L.arel_wave_floats * 4 + 15) / 16 * 16;
+    L.wscr_off = arel_bytes;
+    L.wscr_wave_bytes = kBlockRows * nbin * esz;
+    L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
+    rel_bytes = L.avt_off + (bf16 ? d * nbin * 2 : 0);
   } else {
-    L.cband_stride = kBK + 36;   // 32 + kBK - 1 band rows, padded to a 16-byte multiple
-    L.pband_stride = kBK + 4;
-    L.wave_rel_floats = kWaveRows * (L.cband_stride + L.pband_stride);
-    rel_bytes = kWaves * L.wave_rel_floats * 4;
+    L.deb_wave_floats = kBlockRows * kCbandStride + kBlockRows * kPbandStride;
+    rel_bytes = nw * L.deb_wave_floats * 4;
   }
   L.total = L.rel_off + ((rel_bytes + 15) & ~15);
   return L;

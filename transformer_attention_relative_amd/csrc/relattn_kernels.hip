@@ -6,34 +6,42 @@
 //   [T5B]  "T5 Relative-Position Bias" (liminalml.com)
 //   [DRPE] "DeBERTa > Relative Position Encoding" (mbrenndoerfer.com)
 //
-// Design (one workgroup = 4 wave64s = 128 query rows of one (b, h)):
-//   * Scores are produced transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32): a
-//     lane then owns one query row and 16 keys of each 32-key block, so the
-//     row max / row sum need one cross-lane exchange (lane ^ 32) per tile
-//     and the per-row rescale of the output is a per-lane scalar.
-//   * The output is accumulated transposed too, O^T = V^T P^T, so P leaves
-//     the score accumulator directly as the B operand (no LDS round trip).
-//     V is staged in LDS transposed for that reason.
-//   * The relative term never exists as an L x L array: for each (wave,
-//     key tile) it is either a per-row constant folded into the softmax
-//     exponent (saturated T5 buckets, clipped Shaw / DeBERTa offsets) or it
-//     is written into the MFMA accumulator *before* q.k is accumulated on
-//     top (near-diagonal tiles).  Masked entries enter that accumulator as
-//     -inf, so masking costs nothing in the MFMA loop.
-//   * T5 bucket ids come from host-computed integer thresholds; no log is
-//     evaluated on the GPU ([T5B]: saturation starts at the lower edge of
-//     the last bin).
-//   * Shaw's value term uses the offset-binned softmax mass: every offset
-//     strictly inside the clip window belongs to exactly one key per row, so
-//     its mass is that key's probability; the two clipped bins take the
-//     remainder ([RPE] Shaw section).
-//   * DeBERTa near tiles compute the content-to-position band (Kr rows x Q)
+// Design (a workgroup = NW wave64s; a wave owns QB blocks of 32 query rows
+// of one (b, h)):
+//   * Key/value tiles (64 rows) go straight from global memory into an LDS
+//     ring of stages (global_load_lds_dwordx4), 16-byte chunks XOR-swizzled
+//     per row; no register staging, so the next tiles are in flight while
+//     the current one is used.
+//   * Scores are produced transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
+//     or v_mfma_f32_32x32x2f32 for float32): a lane owns one query row and 16
+//     keys of each 32-key block, so the row max needs one lane^32 exchange per
+//     tile and the output rescale is a per-lane scalar.  One K fragment read
+//     from LDS feeds the QB query blocks of the wave.
+//   * The output is accumulated transposed, O^T = V^T P^T: P leaves the score
+//     accumulator directly as the B operand; the V^T A operand comes from the
+//     row-major V tile through ds_read_b64_tr_b16 (LDS transpose read).
+//   * Online softmax in the exp2 domain with scale*log2(e) folded into one
+//     FMA; the running max is only moved (and the output rescaled) when a new
+//     max exceeds it by more than 2^8, which keeps every exponent <= 8.
+//   * The relative term never exists as an L x L array: per (query block,
+//     key tile) it is a per-row constant folded into the exponent (saturated
+//     T5 buckets, clipped Shaw / DeBERTa offsets) or it is written into the
+//     MFMA accumulator before q.k is accumulated on top (near-diagonal
+//     tiles).  Masked entries enter that accumulator as -inf.
+//   * T5 bucket ids come from host-computed integer thresholds; no log runs
+//     on the GPU ([T5B]: saturation starts at the lower edge of the last bin).
+//   * Shaw's value term: each offset strictly inside the clip window belongs
+//     to exactly one key of a row, so its bin holds that key's probability;
+//     near tiles scatter those probabilities into a per-wave bin tile that is
+//     multiplied by a_V with one more MFMA; the two clipped bins take the rest
+//     of the row mass at the end ([RPE] Shaw section).
+//   * DeBERTa near blocks compute the content-to-position band (Kr rows x Q)
 //     and the position-to-content band (K x Qr rows) with MFMA and gather
-//     them through per-wave LDS; far tiles reduce to a per-row constant plus
-//     a per-key constant ([DRPE] clip-and-shift: every offset beyond +-k uses
-//     a boundary row).
+//     them through per-wave LDS; far blocks reduce to a per-row constant plus
+//     a per-key constant ([DRPE]: every offset beyond +-k uses a boundary row).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "relattn_internal.hpp"
 
@@ -43,21 +51,29 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define RA_NEG_INF (-__builtin_inff())
+#define RA_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders this wave's LDS writes before its later LDS reads (lanes of the same
+// wave read what other lanes wrote).
 __device__ __forceinline__ void wave_lds_fence() {
-  // Orders this wave's LDS writes before its later LDS reads (other lanes of
-  // the same wave read what a lane wrote).
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding, expcnt/lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
 // ----------------------------------------------------------------------------
@@ -109,7 +125,7 @@ __global__ void relattn_index_kernel(IndexArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// MFMA wrappers
+// MFMA helpers and fragments
 // ----------------------------------------------------------------------------
 
 __device__ __forceinline__ f32x16 mma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -119,22 +135,34 @@ __device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ bf16x2 cvt2(float x, float y) {
+  f32x2 v = {x, y};
+  return __builtin_convertvector(v, bf16x2);
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(f32x16 s, int base) {
-  f32x2 p0 = {s[base + 0], s[base + 1]}, p1 = {s[base + 2], s[base + 3]};
-  f32x2 p2 = {s[base + 4], s[base + 5]}, p3 = {s[base + 6], s[base + 7]};
-  bf16x2 c0 = __builtin_convertvector(p0, bf16x2), c1 = __builtin_convertvector(p1, bf16x2);
-  bf16x2 c2 = __builtin_convertvector(p2, bf16x2), c3 = __builtin_convertvector(p3, bf16x2);
+  bf16x2 c0 = cvt2(s[base + 0], s[base + 1]), c1 = cvt2(s[base + 2], s[base + 3]);
+  bf16x2 c2 = cvt2(s[base + 4], s[base + 5]), c3 = cvt2(s[base + 6], s[base + 7]);
   bf16x8 r = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
   return r;
+}
+
+// Sum of the 8 bf16 values with v_dot2c_f32_bf16 (two per instruction).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p[0], p[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p[2], p[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p[4], p[5]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p[6], p[7]}, one, acc, false);
+  return acc;
 }
 
 // In the 32x32 accumulator layout, register i of a lane in half hh holds
 // row 8*(i/4) + 4*hh + (i%4) of the lane's column.
 __device__ __forceinline__ int acc_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
 
-// Row-table fragment: the A operand row (or B operand column) `row` of a
-// table whose rows are `d` contiguous elements.  bf16: elements
-// 16t + 8hh .. +7 for chunk t; fp32: element t + (d/2)*hh.
+// A row-major table row as an MFMA operand (A row or B column): bf16 chunk t
+// holds elements 16t + 8hh .. +7; fp32 element t is d-index t + (d/2)*hh.
 template <bool BF, int D>
 struct TableFrag;
 template <int D>
@@ -143,6 +171,18 @@ struct TableFrag<true, D> {
   __device__ __forceinline__ void load(const bf16* row, int hh) {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) v[t] = *reinterpret_cast<const bf16x8*>(row + 16 * t + 8 * hh);
+  }
+  // row `r` of a swizzled LDS tile (see relattn_internal.hpp)
+  __device__ __forceinline__ void load_lds(const char* tile, int r, int hh) {
+    constexpr int CPR = D / 8, SWZ = (CPR < 8 ? CPR : 8) - 1;
+    const char* rp = tile + r * CPR * 16;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      v[t] = *reinterpret_cast<const bf16x8*>(rp + (((2 * t + hh) ^ (r & SWZ)) * 16));
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) v[t] = {};
   }
 };
 template <int D>
@@ -155,7 +195,37 @@ struct TableFrag<false, D> {
       v[4 * t + 0] = x[0]; v[4 * t + 1] = x[1]; v[4 * t + 2] = x[2]; v[4 * t + 3] = x[3];
     }
   }
+  __device__ __forceinline__ void load_lds(const char* tile, int r, int hh) {
+    constexpr int CPR = D / 4, SWZ = (CPR < 8 ? CPR : 8) - 1;
+    const char* rp = tile + r * CPR * 16;
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(rp + ((((D / 8) * hh + t) ^ (r & SWZ)) * 16));
+      v[4 * t + 0] = x[0]; v[4 * t + 1] = x[1]; v[4 * t + 2] = x[2]; v[4 * t + 3] = x[3];
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int t = 0; t < D / 2; ++t) v[t] = 0.f;
+  }
 };
+
+// a.b over the head dimension, accumulated from zero (the first MFMA takes
+// the inline constant 0 as its accumulator input)
+template <bool BF, int D>
+__device__ __forceinline__ f32x16 mma_frag0(const TableFrag<BF, D>& a, const TableFrag<BF, D>& b) {
+  f32x16 c;
+  if constexpr (BF) {
+    c = mma_bf16(a.v[0], b.v[0], f32x16{});
+#pragma unroll
+    for (int t = 1; t < D / 16; ++t) c = mma_bf16(a.v[t], b.v[t], c);
+  } else {
+    c = mma_f32(a.v[0], b.v[0], f32x16{});
+#pragma unroll
+    for (int t = 1; t < D / 2; ++t) c = mma_f32(a.v[t], b.v[t], c);
+  }
+  return c;
+}
 
 template <bool BF, int D>
 __device__ __forceinline__ f32x16 mma_frag(const TableFrag<BF, D>& a, const TableFrag<BF, D>& b, f32x16 c) {
@@ -169,21 +239,85 @@ __device__ __forceinline__ f32x16 mma_frag(const TableFrag<BF, D>& a, const Tabl
   return c;
 }
 
+// V^T fragment (A operand of O^T = V^T P^T) for the 16-key chunk cc and the
+// 32-wide head-dim block db, read from the row-major swizzled V tile with the
+// LDS transpose read.  ds_read_b64_tr_b16 gives lane (group G = lane/16,
+// index i) the elements e = 0..3 of the 8-byte chunks addressed by lanes
+// 16G + 4e + i/4, each at position i%4.  So lane (G, e, j) addresses key
+// 16cc + 8*half + 4*(G/2) + e at head dims 32db + 16*(G%2) + 4j .. +3, and
+// every lane receives the 4 keys of its MFMA k-slots at head dim
+// 32db + lane%32 -- the same key order as P in the score accumulator.
+template <int D>
+__device__ __forceinline__ bf16x8 load_vt_frag(const char* vtile, int cc, int db, int lane) {
+  constexpr int CPR = D / 8, SWZ = (CPR < 8 ? CPR : 8) - 1;
+  const int G = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
+  const int c = 4 * db + 2 * (G & 1) + (j >> 1);
+  i16x4 r[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int key = 16 * cc + 8 * half + 4 * (G >> 1) + e;
+    const char* addr = vtile + key * CPR * 16 + ((c ^ (key & SWZ)) * 16) + 8 * (j & 1);
+    r[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(addr));
+  }
+  const i16x4 lo = r[0], hi = r[1];
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// float32 V element (key, head dim) of the swizzled row-major tile.
+template <int D>
+__device__ __forceinline__ float load_v_f32(const char* vtile, int key, int dd) {
+  constexpr int CPR = D / 4, SWZ = (CPR < 8 ? CPR : 8) - 1;
+  return *reinterpret_cast<const float*>(vtile + key * CPR * 16 + (((dd >> 2) ^ (key & SWZ)) * 16) +
+                                         (dd & 3) * 4);
+}
+
+// Issue the direct global -> LDS loads of one K tile and one V tile.
+// Instruction `ins` of a tile covers rows ins*RPI .. +RPI-1; lane l fills LDS
+// slot l of that 1 KiB block: row ins*RPI + l/CPR, slot l%CPR, which holds
+// chunk slot ^ (row & SWZ).  Rows past the end of the keys re-read the last
+// key (in bounds; those keys are masked).
+template <bool BF, int D, int NW>
+__device__ __forceinline__ void issue_tile(const char* Kg, const char* Vg, int Lk, int k0,
+                                           char* stage, int tile_bytes, int wave, int lane) {
+  constexpr int ESZ = BF ? 2 : 4, CPR = D * ESZ / 16, SWZ = (CPR < 8 ? CPR : 8) - 1;
+  constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
+#pragma unroll
+  for (int r = 0; r < IPW; ++r) {
+    const int ins = wave + r * NW;
+    if (ins < IPT) {
+      const int row = ins * RPI + lane / CPR;
+      const int slot = lane % CPR;
+      const int chunk = slot ^ (row & SWZ);
+      const int grow = min(k0 + row, Lk - 1);
+      const size_t goff = (size_t)grow * (D * ESZ) + chunk * 16;
+      __builtin_amdgcn_global_load_lds(Kg + goff, (RA_LDS void*)(stage + ins * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vg + goff, (RA_LDS void*)(stage + tile_bytes + ins * 1024), 16, 0, 0);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // The fused forward kernel
 // ----------------------------------------------------------------------------
 
-template <int KIND, bool BF, int D>
-__global__ __launch_bounds__(kThreads, 2) void relattn_fwd_kernel(FwdArgs a) {
+template <int KIND, bool BF, int D, int QB, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a) {
   using T = typename std::conditional<BF, bf16, float>::type;
-  constexpr int NKB = kBK / 32;  // 32-key blocks per tile
-  constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
+  constexpr int NKB = kBK / 32;       // 32-key blocks per tile
+  constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
+  constexpr int RW = 32 * QB;         // query rows per wave
+  constexpr int BQ = RW * NW;         // query rows per workgroup
+  constexpr int NS = num_stages(KIND, BF);
+  constexpr int ESZ = BF ? 2 : 4, CPR = D * ESZ / 16;
+  constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
+  constexpr int LPW = 2 * IPW;        // load instructions per wave per tile
+  constexpr bool EVEN_LOADS = (IPT % NW) == 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const LdsLayout L = lds_layout(KIND, BF, D, a.clip_k, a.lut_n);
-  T* Ks = reinterpret_cast<T*>(smem + L.k_off);
-  T* Vs = reinterpret_cast<T*>(smem + L.v_off);
-  float* rel = reinterpret_cast<float*>(smem + L.rel_off);
+  const LdsLayout L = lds_layout(KIND, BF, D, QB, NW, a.clip_k, a.lut_n);
+  float* relf = reinterpret_cast<float*>(smem + L.rel_off);
 
   // ---- work item (XCD-aware: consecutive logical ids share an L2) ----------
   const int nblk = gridDim.x;
@@ -197,503 +331,570 @@ __global__ __launch_bounds__(kThreads, 2) void relattn_fwd_kernel(FwdArgs a) {
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across the wave; say so, so that everything
+  // derived from it (positions, tile classes) lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
-  const int q0 = qt * kBQ;
-  const int wrow0 = q0 + wave * kWaveRows;       // first row of this wave
-  const int qrow = wrow0 + lq;                    // this lane's query row
-  const int pos = a.q_pos_offset + qrow;          // its absolute position
+  const int q0 = qt * BQ;
+  const int wrow0 = q0 + wave * RW;
   const int pw_min = a.q_pos_offset + wrow0;
-  const int pw_max = pw_min + kWaveRows - 1;
   const bool wave_active = wrow0 < a.Lq;
-  const int pw_max_real = a.q_pos_offset + min(wrow0 + kWaveRows, a.Lq) - 1;
-
-  int kv_lim = a.Lk;
-  if (a.kv_valid_len) kv_lim = max(0, min(kv_lim, a.kv_valid_len[b]));
-  const int wg_pos_max = a.q_pos_offset + min(q0 + kBQ, a.Lq) - 1;
-  const int kv_end = a.causal ? min(kv_lim, wg_pos_max + 1) : kv_lim;
-  const int n_kt = kv_end > 0 ? (kv_end + kBK - 1) / kBK : 0;
-  const int per_split = (n_kt + a.n_splits - 1) / a.n_splits;
-  const int kt_begin = min(n_kt, split * per_split);
-  const int kt_end = min(n_kt, kt_begin + per_split);
-
-  const float c = a.scale_log2;
-  const size_t qkv_head = (size_t)bh;
-  const T* Qg = reinterpret_cast<const T*>(a.q) + qkv_head * a.Lq * D;
-  const T* Kg = reinterpret_cast<const T*>(a.k) + qkv_head * a.Lk * D;
-  const T* Vg = reinterpret_cast<const T*>(a.v) + qkv_head * a.Lk * D;
-
-  // ---- Q fragment (B operand of S^T = K Q^T), held for the whole loop ------
-  TableFrag<BF, D> qf;
-  if (qrow < a.Lq) {
-    qf.load(Qg + (size_t)qrow * D, hh);
-  } else {
+  const int pw_max_real = a.q_pos_offset + min(wrow0 + RW, a.Lq) - 1;
+  int qrow[QB], pos[QB];
 #pragma unroll
-    for (int t = 0; t < (BF ? D / 16 : D / 2); ++t) qf.v[t] = {};
+  for (int qb = 0; qb < QB; ++qb) {
+    qrow[qb] = wrow0 + 32 * qb + lq;
+    pos[qb] = a.q_pos_offset + qrow[qb];
   }
 
-  // ---- per-kind prologue -----------------------------------------------------
-  float bias_left_raw = 0.f, bias_right_raw = 0.f;  // T5 saturated buckets / scale
-  float shaw_right = 0.f;                            // Shaw: q.(a_K[2k] - a_K[0])
-  float crow_lo = 0.f, crow_hi = 0.f;                // DeBERTa: q.Kr[0], q.Kr[2k-1]
-  float* arel = nullptr;
-  float* slog = nullptr;
-  float* cband = nullptr;
-  float* pband = nullptr;
+  const float c = a.scale_log2;
+  const float thr_raw = 8.0f / c;  // lazy rescale threshold in raw score units
+  const T* Qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * a.Lq * D;
+  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + (size_t)bh * a.Lk * D);
+  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + (size_t)bh * a.Lk * D);
+  const int wg_pos_max = a.q_pos_offset + min(q0 + BQ, a.Lq) - 1;
   const int ck = a.clip_k;
 
+  // ---- register loads first (Q fragments, the kind's small tables): the
+  // key/value stream is issued after them, so waiting for these values never
+  // waits for the stream (vector-memory counters retire in order) ----------
+  TableFrag<BF, D> qf[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (qrow[qb] < a.Lq) qf[qb].load(Qg + (size_t)qrow[qb] * D, hh);
+    else qf[qb].zero();
+  }
+  constexpr int LUT_EARLY = 8;  // offset-table entries per thread fetched early
+  float lut_early[LUT_EARLY];
+  float bias_left_raw = 0.f, bias_right_raw = 0.f;  // T5 saturated buckets / scale
+  constexpr int SHAW_RB = 3;                          // blocks of 32 a_K rows (k <= 32)
+  TableFrag<BF, D> krow[KIND == 1 ? SHAW_RB : 1];     // Shaw a_K rows / DeBERTa Kr rows
+  constexpr int AVT_EARLY = 8;
+  T avt_early[AVT_EARLY];
+  const float inv_scale = 1.f / a.scale;
   if constexpr (KIND == 0) {
     const float* tab = reinterpret_cast<const float*>(a.table);
-    const float inv_scale = 1.f / a.scale;
-    for (int e = tid; e < a.lut_n; e += kThreads) {
-      const int bk = t5_bucket_dev(a.lut_lo + e, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
-      rel[e] = tab[bk * a.H + h] * inv_scale;
+#pragma unroll
+    for (int i = 0; i < LUT_EARLY; ++i) {
+      const int e = tid + i * 64 * NW;
+      lut_early[i] = 0.f;
+      if (e < 4 * L.lut_stride) {
+        const int cpy = e / L.lut_stride, x = e - cpy * L.lut_stride + cpy;
+        if (x < a.lut_n) {
+          const int bk = t5_bucket_dev(a.lut_lo + x, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
+          lut_early[i] = tab[bk * a.H + h];
+        }
+      }
     }
     const int bl = t5_bucket_dev(-(1 << 30), a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
     const int br = t5_bucket_dev(1 << 30, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
     bias_left_raw = tab[bl * a.H + h] * inv_scale;
     bias_right_raw = tab[br * a.H + h] * inv_scale;
   } else if constexpr (KIND == 1) {
-    // arel[q][r] = q.a_K[r] - q.a_K[0] for r in 0..2k, by MFMA over blocks of
-    // 32 table rows; subtracting the r = 0 value is softmax-neutral and makes
-    // every key beyond -k contribute exactly zero.
-    arel = rel + wave * L.wave_rel_floats;
-    slog = arel + kWaveRows * L.arel_stride;
     const T* ak = reinterpret_cast<const T*>(a.table);
     const int nrow = 2 * ck + 1;
-    float base0 = 0.f;
-    for (int rb = 0; rb * 32 < nrow; ++rb) {
-      TableFrag<BF, D> af;
-      af.load(ak + (size_t)min(rb * 32 + lq, nrow - 1) * D, hh);
-      f32x16 acc = {};
-      acc = mma_frag<BF, D>(af, qf, acc);
-      if (rb == 0) base0 = __shfl(acc[0], lq);  // row 0 sits in lane lq, register 0
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rb * 32 + acc_row(i, hh);
-        if (r < nrow) arel[lq * L.arel_stride + r] = acc[i] - base0;
+    for (int rb = 0; rb < SHAW_RB; ++rb)
+      if (rb * 32 < nrow) krow[rb].load(ak + (size_t)min(rb * 32 + lq, nrow - 1) * D, hh);
+    if constexpr (BF) {
+      const int nb = shaw_bin_slots(ck);
+      const T* av = reinterpret_cast<const T*>(a.table2);
+#pragma unroll
+      for (int i = 0; i < AVT_EARLY; ++i) {
+        const int e = tid + i * 64 * NW;
+        avt_early[i] = (T)0.f;
+        if (e < D * nb) {
+          const int dd = e / nb, r = e - dd * nb;
+          if (r < 2 * ck - 1) avt_early[i] = av[(size_t)(r + 1) * D + dd];
+        }
       }
     }
-    for (int r = hh; r < L.slog_stride; r += 2) slog[lq * L.slog_stride + r] = RA_NEG_INF;
-    wave_lds_fence();
-    shaw_right = arel[lq * L.arel_stride + 2 * ck];
   } else {
-    cband = rel + wave * L.wave_rel_floats;
-    pband = cband + kWaveRows * L.cband_stride;
     const T* kr = reinterpret_cast<const T*>(a.table);
-    TableFrag<BF, D> af;
     const int u = (lq == 1) ? 2 * ck - 1 : 0;
-    af.load(kr + ((size_t)u * a.H + h) * D, hh);
-    f32x16 acc = {};
-    acc = mma_frag<BF, D>(af, qf, acc);
-    crow_lo = __shfl(acc[0], lq);
-    crow_hi = __shfl(acc[1], lq);
+    krow[0].load(kr + ((size_t)u * a.H + h) * D, hh);
   }
 
-  // ---- K/V tile staging (global -> registers -> LDS) -----------------------
-  constexpr int VEC = BF ? 8 : 4;                 // elements per 16-byte load
-  constexpr int K_CHUNKS = kBK * D / VEC;
-  constexpr int K_PER_T = (K_CHUNKS + kThreads - 1) / kThreads;
-  constexpr int V_UNITS = BF ? (kBK / 2) * (D / 8) : kBK * D / 4;
-  constexpr int V_PER_T = (V_UNITS + kThreads - 1) / kThreads;
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[V_PER_T][BF ? 2 : 1];
+  // ---- start streaming the first key tiles --------------------------------
+  // Without a key split the first tiles are known before the valid length is
+  // read (tiles past it are loaded in bounds and never used).
+  const int reach0 = a.causal ? min(a.Lk, wg_pos_max + 1) : a.Lk;
+  const int n_pre0 = a.n_splits == 1 ? (reach0 + kBK - 1) / kBK : 0;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < n_pre0)
+      issue_tile<BF, D, NW>(Kg, Vg, a.Lk, s * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
 
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * kBK;
+  int kv_lim = a.Lk;
+  if (a.kv_valid_len) kv_lim = max(0, min(kv_lim, a.kv_valid_len[b]));
+  const int kv_end = a.causal ? min(kv_lim, wg_pos_max + 1) : kv_lim;
+  const int n_kt = kv_end > 0 ? (kv_end + kBK - 1) / kBK : 0;
+  const int per_split = (n_kt + a.n_splits - 1) / a.n_splits;
+  const int kt_begin = min(n_kt, split * per_split);
+  const int kt_end = min(n_kt, kt_begin + per_split);
+  const int n_my = kt_end - kt_begin;
+  if (a.n_splits > 1) {
 #pragma unroll
-    for (int r = 0; r < K_PER_T; ++r) {
-      const int id = tid + r * kThreads;
-      const int key = id / (D / VEC), ch = id % (D / VEC);
-      u32x4 x = {};
-      if (id < K_CHUNKS && k0 + key < a.Lk)
-        x = *reinterpret_cast<const u32x4*>(Kg + (size_t)(k0 + key) * D + ch * VEC);
-      kreg[r] = x;
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < n_my)
+        issue_tile<BF, D, NW>(Kg, Vg, a.Lk, (kt_begin + s) * kBK, smem + s * L.stage_bytes,
+                              L.tile_bytes, wave, lane);
+  }
+
+  // ---- per-kind prologue (LDS tables) ---------------------------------------
+  float shaw_right[QB];                              // Shaw: q.(a_K[2k] - a_K[0])
+  float crow_lo[QB], crow_hi[QB];                    // DeBERTa: q.Kr[0], q.Kr[2k-1]
+  float* arel = nullptr;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = crow_lo[qb] = crow_hi[qb] = 0.f;
+
+  if constexpr (KIND == 0) {
+    // four copies of bias[offset]/scale, copy c shifted by c entries
+#pragma unroll
+    for (int i = 0; i < LUT_EARLY; ++i) {
+      const int e = tid + i * 64 * NW;
+      if (e < 4 * L.lut_stride) relf[e] = lut_early[i] * inv_scale;
     }
+    const float* tab = reinterpret_cast<const float*>(a.table);
+    for (int e = tid + LUT_EARLY * 64 * NW; e < 4 * L.lut_stride; e += 64 * NW) {
+      const int cpy = e / L.lut_stride, x = e - cpy * L.lut_stride + cpy;
+      float val = 0.f;
+      if (x < a.lut_n) {
+        const int bk = t5_bucket_dev(a.lut_lo + x, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
+        val = tab[bk * a.H + h] * inv_scale;
+      }
+      relf[e] = val;
+    }
+  } else if constexpr (KIND == 1) {
+    // arel[row][r] = q.a_K[r] - q.a_K[0], r = 0..2k, by MFMA over blocks of 32
+    // table rows; subtracting the r = 0 value is softmax-neutral and makes
+    // every key beyond -k contribute exactly zero.
+    arel = relf + wave * L.arel_wave_floats;
+    const int nrow = 2 * ck + 1;
 #pragma unroll
-    for (int r = 0; r < V_PER_T; ++r) {
-      const int id = tid + r * kThreads;
-      if constexpr (BF) {
-        const int pr = id / (D / 8), ch = id % (D / 8);
-        u32x4 x0 = {}, x1 = {};
-        if (id < V_UNITS) {
-          if (k0 + 2 * pr < a.Lk) x0 = *reinterpret_cast<const u32x4*>(Vg + (size_t)(k0 + 2 * pr) * D + ch * 8);
-          if (k0 + 2 * pr + 1 < a.Lk) x1 = *reinterpret_cast<const u32x4*>(Vg + (size_t)(k0 + 2 * pr + 1) * D + ch * 8);
+    for (int qb = 0; qb < QB; ++qb) {
+      float base0 = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < SHAW_RB; ++rb) {
+        if (rb * 32 >= nrow) break;
+        const f32x16 acc = mma_frag0<BF, D>(krow[rb], qf[qb]);
+        if (rb == 0) base0 = __shfl(acc[0], lq);  // row 0 sits in lane lq, register 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = rb * 32 + acc_row(i, hh);
+          if (r < nrow) arel[(32 * qb + lq) * L.arel_stride + r] = acc[i] - base0;
         }
-        vreg[r][0] = x0;
-        vreg[r][1] = x1;
-      } else {
-        const int key = id / (D / 4), ch = id % (D / 4);
-        u32x4 x = {};
-        if (id < V_UNITS && k0 + key < a.Lk)
-          x = *reinterpret_cast<const u32x4*>(Vg + (size_t)(k0 + key) * D + ch * 4);
-        vreg[r][0] = x;
       }
     }
-  };
-  auto store_tile = [&](int buf) {
-    T* ks = Ks + buf * kBK * L.k_stride;
+    wave_lds_fence();
 #pragma unroll
-    for (int r = 0; r < K_PER_T; ++r) {
-      const int id = tid + r * kThreads;
-      const int key = id / (D / VEC), ch = id % (D / VEC);
-      if (id < K_CHUNKS) *reinterpret_cast<u32x4*>(ks + key * L.k_stride + ch * VEC) = kreg[r];
-    }
+    for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = arel[(32 * qb + lq) * L.arel_stride + 2 * ck];
     if constexpr (BF) {
-      T* vt = Vs + buf * D * L.v_stride;
+      // a_V^T for the in-window bins: avt[d][r'] = a_V[r' + 1][d], r' < 2k - 1
+      const int nb = shaw_bin_slots(ck);
+      T* avt = reinterpret_cast<T*>(smem + L.rel_off + L.avt_off);
+      const T* av = reinterpret_cast<const T*>(a.table2);
 #pragma unroll
-      for (int r = 0; r < V_PER_T; ++r) {
-        const int id = tid + r * kThreads;
-        const int pr = id / (D / 8), ch = id % (D / 8);
-        if (id < V_UNITS) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (vreg[r][0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t hi = (vreg[r][1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            *reinterpret_cast<uint32_t*>(vt + (ch * 8 + e) * L.v_stride + 2 * pr) = lo | (hi << 16);
-          }
-        }
+      for (int i = 0; i < AVT_EARLY; ++i) {
+        const int e = tid + i * 64 * NW;
+        if (e < D * nb) avt[e] = avt_early[i];
       }
-    } else {
-      T* vs = Vs + buf * kBK * L.v_stride;
-#pragma unroll
-      for (int r = 0; r < V_PER_T; ++r) {
-        const int id = tid + r * kThreads;
-        const int key = id / (D / 4), ch = id % (D / 4);
-        if (id < V_UNITS) *reinterpret_cast<u32x4*>(vs + key * L.v_stride + ch * 4) = vreg[r][0];
+      for (int e = tid + AVT_EARLY * 64 * NW; e < D * nb; e += 64 * NW) {
+        const int dd = e / nb, r = e - dd * nb;
+        avt[e] = r < 2 * ck - 1 ? av[(size_t)(r + 1) * D + dd] : (T)0.f;
       }
     }
-  };
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const f32x16 acc = mma_frag0<BF, D>(krow[0], qf[qb]);
+      crow_lo[qb] = __shfl(acc[0], lq);
+      crow_hi[qb] = __shfl(acc[1], lq);
+    }
+  }
 
   // ---- running state ------------------------------------------------------
-  f32x16 o[NDB];
+  f32x16 o[QB][NDB];
+  float m_run[QB], l_run[QB], lr_run[QB], win_run[QB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = {};
-  float m_run = RA_NEG_INF;  // raw-score running max (shared by both halves)
-  float l_run = 0.f;         // this lane's partial row sum
-  float lr_run = 0.f;        // Shaw: partial mass of keys at offset >= k
-
-  if (kt_begin < kt_end) {
-    load_tile(kt_begin);
-    store_tile(0);
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[qb][db] = {};
+    m_run[qb] = RA_NEG_INF;  // raw-score reference max (both halves agree)
+    l_run[qb] = 0.f;         // this lane's partial row sum
+    lr_run[qb] = 0.f;        // Shaw: partial mass of keys at offset >= k
+    win_run[qb] = 0.f;       // Shaw: partial mass of keys inside the clip window
   }
-  __syncthreads();
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) load_tile(kt + 1);
+  for (int r = 0; r < n_my; ++r) {
+    const int kt = kt_begin + r;
+    if constexpr (NS >= 3 && EVEN_LOADS) {
+      // tiles newer than r that may still be in flight: min(NS - 2, n_my - 1 - r)
+      const int newer = min(NS - 2, n_my - 1 - r);
+      if (NS >= 4 && newer >= 2) wait_vmcnt<(NS >= 4 ? 2 * LPW : 0)>();
+      else if (newer >= 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     const int k0 = kt * kBK;
-
-    if (wave_active && k0 <= (a.causal ? pw_max_real : 0x7fffffff)) {
-      const T* ks = Ks + buf * kBK * L.k_stride;
-      f32x16 s[NKB];
-      float b_raw = 0.f;
-      bool shaw_near = false, shaw_far_right = false;
-
-      // (1) relative term into the accumulator, or into b_raw
-      if constexpr (KIND == 0) {
-        const int omin = k0 - pw_max, omax = k0 + kBK - 1 - pw_min;
-        if (omax <= -a.t5_lsat) {
+    const bool active = wave_active && !(a.causal && k0 > pw_max_real);
+    // DeBERTa per-key constants of clipped blocks are requested before the
+    // next tiles, so waiting for them never waits for the prefetch
+    f32x4 colv[QB][NKB][4];
+    if constexpr (KIND == 2) {
+      if (active) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) s[kb] = {};
-          b_raw = bias_left_raw;
-        } else if (omin >= a.t5_rsat) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) s[kb] = {};
-          b_raw = bias_right_raw;
-        } else {
-          const float* lut = rel + (k0 - pos - a.lut_lo);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = lut[32 * kb + acc_row(i, hh)];
-        }
-      } else if constexpr (KIND == 1) {
-        const int omin = k0 - pw_max, omax = k0 + kBK - 1 - pw_min;
-        if (omax <= -ck) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) s[kb] = {};
-        } else if (omin >= ck) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) s[kb] = {};
-          b_raw = shaw_right;
-          shaw_far_right = true;
-        } else {
-          shaw_near = true;
-          const float* ar = arel + lq * L.arel_stride;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = ar[shaw_row_dev(k0 + 32 * kb + acc_row(i, hh) - pos, ck)];
-        }
-      } else {
-        const int tmin = pw_min - (k0 + kBK - 1), tmax = pw_max - k0;  // t = query - key
-        if (tmin >= ck || tmax <= -ck) {
-          const int side = tmin >= ck ? 0 : 1;
-          b_raw = side == 0 ? crow_hi : crow_lo;
-          const float* cc = a.colc + ((size_t)side * a.B * a.H + bh) * a.Lk_pad + k0;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4 x = *reinterpret_cast<const f32x4*>(cc + 32 * kb + 8 * g + 4 * hh);
-              s[kb][4 * g + 0] = x[0]; s[kb][4 * g + 1] = x[1];
-              s[kb][4 * g + 2] = x[2]; s[kb][4 * g + 3] = x[3];
-            }
-        } else {
-          const T* kr = reinterpret_cast<const T*>(a.table);
-          const T* qr = reinterpret_cast<const T*>(a.table2);
-          // content-to-position band: rows t = T0 + m, m in [0, 32 + kBK - 1)
-          const int T0 = pw_min - (k0 + kBK - 1);
-#pragma unroll
-          for (int tb = 0; tb < NKB + 1; ++tb) {
-            TableFrag<BF, D> af;
-            const int u = deberta_delta_dev(T0 + 32 * tb + lq, ck);
-            af.load(kr + ((size_t)u * a.H + h) * D, hh);
-            f32x16 acc = {};
-            acc = mma_frag<BF, D>(af, qf, acc);
-            float* dst = cband + lq * L.cband_stride + 32 * tb + 4 * hh;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-              *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
-            }
-          }
-          // position-to-content band per 32-key block: columns n, t = T1 + n,
-          // Qr row delta(key, query) = clip(-t) + k; scattered to [query][key]
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
-            TableFrag<BF, D> kf;
-            kf.load(ks + (32 * kb + lq) * L.k_stride, hh);
-            const int T1 = pw_min - (k0 + 32 * kb) - 31;
+            const int pq_min = pw_min + 32 * qb, j0 = k0 + 32 * kb;
+            const int tmin = pq_min - (j0 + 31), tmax = pq_min + 31 - j0;
+            const int side = tmin >= ck ? 0 : (tmax <= -ck ? 1 : -1);
+            if (side >= 0) {
+              const float* cc = a.colc + ((size_t)side * a.B * a.H + bh) * a.Lk_pad + j0;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) colv[qb][kb][g] = *reinterpret_cast<const f32x4*>(cc + 8 * g + 4 * hh);
+            }
+          }
+      }
+    }
+    if (r + NS - 1 < n_my)
+      issue_tile<BF, D, NW>(Kg, Vg, a.Lk, (kt + NS - 1) * kBK, smem + ((r + NS - 1) % NS) * L.stage_bytes,
+                            L.tile_bytes, wave, lane);
+    const char* ktile = smem + (r % NS) * L.stage_bytes;
+    const char* vtile = ktile + L.tile_bytes;
+    if (!active) continue;
+
+    f32x16 s[QB][NKB];
+    float b_raw[QB];
+    bool near[QB], far_right[QB];
+    int deb_side[QB];  // DeBERTa: 0 far-left tile, 1 far-right tile, -1 mixed
+    const float* lutp[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      b_raw[qb] = 0.f;
+      near[qb] = far_right[qb] = false;
+      deb_side[qb] = -1;
+      lutp[qb] = nullptr;
+      const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
+      const int omin = k0 - pq_max, omax = k0 + kBK - 1 - pq_min;  // key - query
+      if constexpr (KIND == 0) {
+        if (omax <= -a.t5_lsat) b_raw[qb] = bias_left_raw;
+        else if (omin >= a.t5_rsat) b_raw[qb] = bias_right_raw;
+        else {
+          near[qb] = true;
+          const int x0 = k0 - pos[qb] - a.lut_lo;  // table index of this lane's first key
+          const int cp = x0 & 3;
+          lutp[qb] = relf + cp * L.lut_stride + (x0 - cp);
+        }
+      } else if constexpr (KIND == 1) {
+        if (omin >= ck) {
+          b_raw[qb] = shaw_right[qb];
+          far_right[qb] = true;
+        } else if (omax > -ck) {
+          near[qb] = true;
+        }
+      } else {
+        if (-omax >= ck) { deb_side[qb] = 0; b_raw[qb] = crow_hi[qb]; }       // every query - key >= k
+        else if (-omin <= -ck) { deb_side[qb] = 1; b_raw[qb] = crow_lo[qb]; } // every query - key <= -k
+      }
+    }
+
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int j0 = k0 + 32 * kb;
+      TableFrag<BF, D> kf;
+      kf.load_lds(ktile, 32 * kb + lq, hh);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
+        // (1)+(2) relative term into the accumulator, then S^T += K Q^T on top
+        // (far blocks start from the MFMA's zero accumulator input)
+        if constexpr (KIND == 0) {
+          if (near[qb]) {
+            f32x16 init;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(lutp[qb] + 32 * kb + 8 * g + 4 * hh);
+              init[4 * g + 0] = x[0]; init[4 * g + 1] = x[1];
+              init[4 * g + 2] = x[2]; init[4 * g + 3] = x[3];
+            }
+            s[qb][kb] = mma_frag<BF, D>(kf, qf[qb], init);
+          } else {
+            s[qb][kb] = mma_frag0<BF, D>(kf, qf[qb]);
+          }
+        } else if constexpr (KIND == 1) {
+          if (near[qb]) {
+            const float* ar = arel + (32 * qb + lq) * L.arel_stride;
+            f32x16 init;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) init[i] = ar[shaw_row_dev(j0 + acc_row(i, hh) - pos[qb], ck)];
+            s[qb][kb] = mma_frag<BF, D>(kf, qf[qb], init);
+          } else {
+            s[qb][kb] = mma_frag0<BF, D>(kf, qf[qb]);
+          }
+        } else {
+          const int tmin = pq_min - (j0 + 31), tmax = pq_max - j0;  // query - key over the block
+          int side = -1;
+          if (tmin >= ck) side = 0;
+          else if (tmax <= -ck) side = 1;
+          if (side >= 0) {
+            // per-key constant k_j.Qr[0] (side 0) or k_j.Qr[2k-1] (side 1); the
+            // per-row constant is folded into the exponent for whole-tile
+            // sides, else added here
+            const float add = deb_side[qb] >= 0 ? 0.f : (side == 0 ? crow_hi[qb] : crow_lo[qb]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 x = colv[qb][kb][g];
+              s[qb][kb][4 * g + 0] = x[0] + add; s[qb][kb][4 * g + 1] = x[1] + add;
+              s[qb][kb][4 * g + 2] = x[2] + add; s[qb][kb][4 * g + 3] = x[3] + add;
+            }
+          } else {
+            float* cband = relf + wave * L.deb_wave_floats;
+            float* pband = cband + kBlockRows * kCbandStride;
+            const T* kr = reinterpret_cast<const T*>(a.table);
+            const T* qr = reinterpret_cast<const T*>(a.table2);
+            const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
+            // content-to-position: rows Kr[delta(T0 + m)], columns = queries
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+              TableFrag<BF, D> af;
+              af.load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
+              f32x16 acc = {};
+              acc = mma_frag<BF, D>(af, qf[qb], acc);
+              float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+                *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
+              }
+            }
+            // position-to-content: rows = keys, columns n <-> query - key =
+            // T0 + n, Qr row delta(key - query); scattered to [query][key]
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
               const int n = 32 * nb + lq;
-              TableFrag<BF, D> bf;
-              const int u = deberta_delta_dev(-(T1 + n), ck);
-              bf.load(qr + ((size_t)u * a.H + h) * D, hh);
+              TableFrag<BF, D> bfr;
+              bfr.load(qr + ((size_t)deberta_delta_dev(-(T0 + n), ck) * a.H + h) * D, hh);
               f32x16 acc = {};
-              acc = mma_frag<BF, D>(kf, bf, acc);
+              acc = mma_frag<BF, D>(kf, bfr, acc);
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int jl = acc_row(i, hh);
                 const int sq = n + jl - 31;
-                if (sq >= 0 && sq < 32) pband[sq * L.pband_stride + 32 * kb + jl] = acc[i];
+                if (sq >= 0 && sq < 32) pband[sq * kPbandStride + jl] = acc[i];
               }
             }
-          }
-          wave_lds_fence();
-          const float* crow = cband + lq * L.cband_stride + (pos - pw_min) + (kBK - 1);
-          const float* prow = pband + lq * L.pband_stride;
+            wave_lds_fence();
+            const float* crow = cband + lq * kCbandStride + (pos[qb] - pq_min) + 31;
+            const float* prow = pband + lq * kPbandStride;
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 pc = *reinterpret_cast<const f32x4*>(prow + 8 * g + 4 * hh);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int jt = 32 * kb + acc_row(i, hh);
-              s[kb][i] = crow[-jt] + prow[jt];
+              for (int e = 0; e < 4; ++e) s[qb][kb][4 * g + e] = crow[-(8 * g + 4 * hh + e)] + pc[e];
             }
-          wave_lds_fence();  // the next tile overwrites both bands
+            wave_lds_fence();  // the next block overwrites both bands
+          }
+          s[qb][kb] = mma_frag<BF, D>(kf, qf[qb], s[qb][kb]);
         }
-      }
-
-      // (2) masks: -inf enters the accumulator before q.k is added
-      const bool need_mask = (a.causal && k0 + kBK - 1 > pw_min) || (k0 + kBK > kv_lim);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        // (3) masks: hidden keys become -inf (only on blocks that touch the
+        // causal diagonal or the end of the valid keys)
+        if ((a.causal && j0 + 31 > pq_min) || (j0 + 32 > kv_lim)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = k0 + 32 * kb + acc_row(i, hh);
-            if (j >= kv_lim || (a.causal && j > pos)) s[kb][i] = RA_NEG_INF;
+            const int j = j0 + acc_row(i, hh);
+            if (j >= kv_lim || (a.causal && j > pos[qb])) s[qb][kb][i] = RA_NEG_INF;
           }
-      }
-
-      // (3) S^T += K Q^T
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        TableFrag<BF, D> kf;
-        kf.load(ks + (32 * kb + lq) * L.k_stride, hh);
-        s[kb] = mma_frag<BF, D>(kf, qf, s[kb]);
-      }
-
-      // (4) Shaw: remember the logits of keys strictly inside the clip window
-      float lr_tile = 0.f;
-      if constexpr (KIND == 1) {
-        if (shaw_near) {
-          float* sl = slog + lq * L.slog_stride;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int off = k0 + 32 * kb + acc_row(i, hh) - pos;
-              if (off > -ck && off < ck) sl[off + ck - 1] = s[kb][i] * c;
-            }
         }
       }
+    }
 
-      // (5) online softmax (exp2 domain; scale*log2e folded into one FMA)
+    // (4) online softmax per query block, P to the PV operand layout
+    using PFrag = typename std::conditional<BF, bf16x8, float>::type;
+    PFrag pf[QB][BF ? kBK / 16 : 1];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = RA_NEG_INF;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx + b_raw);
-      const float m_use = (m_new == RA_NEG_INF) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * c);
-      const float off = (b_raw - m_use) * c;
-      float lsum = 0.f;
+      const float cand = mx + b_raw[qb];
+      const bool need = cand > m_run[qb] + thr_raw;
+      if (__any(need)) {
+        const float m_new = need ? cand : m_run[qb];
+        const float alpha = fast_exp2((m_run[qb] - m_new) * c);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+        l_run[qb] *= alpha;
+        lr_run[qb] *= alpha;
+        win_run[qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float m_use = (m_run[qb] == RA_NEG_INF) ? 0.f : m_run[qb];
+      const float off = (b_raw[qb] - m_use) * c;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[kb][i], c, off));
-          s[kb][i] = p;
-          lsum += p;
-        }
-      if constexpr (KIND == 1) {
-        if (shaw_far_right) {
-          lr_tile = lsum;
-        } else if (shaw_near) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (k0 + 32 * kb + acc_row(i, hh) - pos >= ck) lr_tile += s[kb][i];
-        }
-        lr_run = lr_run * alpha + lr_tile;
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-
-      // (6) O^T += V^T P^T
+        for (int i = 0; i < 16; ++i) s[qb][kb][i] = fast_exp2(fmaf(s[qb][kb][i], c, off));
+      float lsum = 0.f;
       if constexpr (BF) {
-        const T* vt = Vs + buf * D * L.v_stride;
 #pragma unroll
         for (int cc = 0; cc < kBK / 16; ++cc) {
-          const bf16x8 pf = pack_bf16x8(s[cc >> 1], 8 * (cc & 1));
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const T* vr = vt + (32 * db + lq) * L.v_stride + 16 * cc + 4 * hh;
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 8);
-            const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[db] = mma_bf16(vf, pf, o[db]);
-          }
+          pf[qb][cc] = pack_bf16x8(s[qb][cc >> 1], 8 * (cc & 1));
+          lsum = sum_bf16x8(pf[qb][cc], lsum);
         }
       } else {
-        const T* vs = Vs + buf * kBK * L.v_stride;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int cc = 0; cc < 16; ++cc) {
-            const int key = 32 * kb + acc_row(cc, hh);
+          for (int i = 0; i < 16; ++i) lsum += s[qb][kb][i];
+      }
+      l_run[qb] += lsum;
+
+      // (5) Shaw: bins of this tile
+      if constexpr (KIND == 1) {
+        if (far_right[qb]) {
+          lr_run[qb] += lsum;
+        } else if (near[qb]) {
+          const int nbin = shaw_bin_slots(ck);
+          T* wsc = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes);
+          T* wrow = wsc + lq * nbin;
+          for (int x = hh * (nbin / 2); x < (hh + 1) * (nbin / 2); ++x) wrow[x] = (T)0.f;
+          wave_lds_fence();
+          float win = 0.f, lr = 0.f;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              o[db] = mma_f32(vs[key * L.v_stride + 32 * db + lq], s[kb][cc], o[db]);
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int offk = k0 + 32 * kb + acc_row(i, hh) - pos[qb];
+              float pv;
+              if constexpr (BF) pv = (float)pf[qb][2 * kb + (i >> 3)][i & 7];
+              else pv = s[qb][kb][i];
+              if (offk > -ck && offk < ck) {
+                wrow[offk + ck - 1] = (T)pv;
+                win += pv;
+              } else if (offk >= ck) {
+                lr += pv;
+              }
+            }
+          win_run[qb] += win;
+          lr_run[qb] += lr;
+          wave_lds_fence();
+          if constexpr (BF) {
+            const bf16* avt = reinterpret_cast<const bf16*>(smem + L.rel_off + L.avt_off);
+            for (int cb = 0; cb < nbin / 16; ++cb) {
+              const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 16 * cb + 8 * hh);
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(avt + (32 * db + lq) * nbin + 16 * cb + 8 * hh);
+                o[qb][db] = mma_bf16(vf, wf, o[qb][db]);
+              }
+            }
+          } else {
+            const float* av = reinterpret_cast<const float*>(a.table2);
+            for (int cb = 0; cb < nbin / 2; ++cb) {
+              const int rr = 2 * cb + hh;
+              const float wv = wrow[rr];
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const float vv = rr < 2 * ck - 1 ? av[(size_t)(rr + 1) * D + 32 * db + lq] : 0.f;
+                o[qb][db] = mma_f32(vv, wv, o[qb][db]);
+              }
+            }
           }
+          wave_lds_fence();  // the next near tile rewrites the bin tile
+        }
       }
     }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    // (6) O^T += V^T P^T; one V fragment feeds every query block
+    if constexpr (BF) {
+#pragma unroll
+      for (int cc = 0; cc < kBK / 16; ++cc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 vf = load_vt_frag<D>(vtile, cc, db, lane);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mma_bf16(vf, pf[qb][cc], o[qb][db]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+          const int key = 32 * kb + acc_row(cc, hh);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const float vv = load_v_f32<D>(vtile, key, 32 * db + lq);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mma_f32(vv, s[qb][kb][cc], o[qb][db]);
+          }
+        }
+    }
   }
 
   // ---- epilogue -------------------------------------------------------------
+  wait_vmcnt<0>();  // no tile load may still be writing LDS when the wave ends
   if (!wave_active) return;
-  float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float m_use = (m_run == RA_NEG_INF) ? 0.f : m_run;
-
-  if constexpr (KIND == 1) {
-    // value term: bins inside the clip window hold single-key masses; bin 0
-    // and bin 2k take what remains of the row mass.
-    const T* av = reinterpret_cast<const T*>(a.table2);
-    const float lr_tot = lr_run + __shfl_xor(lr_run, 32);
-    const float* sl = slog + lq * L.slog_stride;
-    const int nin = 2 * ck - 1;  // bins 1 .. 2k-1
-    float wsum = 0.f;
-    if constexpr (BF) {
-      for (int cc = 0; cc * 16 < nin; ++cc) {
-        float w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 16 * cc + 8 * hh + e;
-          w[e] = r < nin ? fast_exp2(sl[r] - m_use * c) : 0.f;
-          wsum += w[e];
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const float m_use = (m_run[qb] == RA_NEG_INF) ? 0.f : m_run[qb];
+    if constexpr (KIND == 1) {
+      // bins 0 and 2k take the row mass not held by the in-window bins
+      const T* av = reinterpret_cast<const T*>(a.table2);
+      const float lr_tot = lr_run[qb] + __shfl_xor(lr_run[qb], 32);
+      const float w_in = win_run[qb] + __shfl_xor(win_run[qb], 32);
+      const float w0 = l_tot - w_in - lr_tot;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int dd = 32 * db + acc_row(i, hh);
+          o[qb][db][i] += w0 * (float)av[dd] + lr_tot * (float)av[(size_t)(2 * ck) * D + dd];
         }
-        f32x16 tmp = {w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
-        const bf16x8 wf = pack_bf16x8(tmp, 0);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          bf16x8 vf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 16 * cc + 8 * hh + e;
-            vf[e] = r < nin ? av[(size_t)(r + 1) * D + 32 * db + lq] : (bf16)0.f;
-          }
-          o[db] = mma_bf16(vf, wf, o[db]);
-        }
-      }
-    } else {
-      for (int cc = 0; cc * 2 < nin; ++cc) {
-        const int r = 2 * cc + hh;
-        const float w = r < nin ? fast_exp2(sl[r] - m_use * c) : 0.f;
-        wsum += w;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const float vv = r < nin ? av[(size_t)(r + 1) * D + 32 * db + lq] : 0.f;
-          o[db] = mma_f32(vv, w, o[db]);
-        }
-      }
     }
-    const float w_in = wsum + __shfl_xor(wsum, 32);
-    const float w0 = l_tot - w_in - lr_tot;
+    if (qrow[qb] >= a.Lq) continue;
+    if (a.n_splits == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      T* og = reinterpret_cast<T*>(a.out) + ((size_t)bh * a.Lq + qrow[qb]) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int dd = 32 * db + acc_row(i, hh);
-        o[db][i] += w0 * (float)av[dd] + lr_tot * (float)av[(size_t)(2 * ck) * D + dd];
-      }
-  }
-
-  if (qrow >= a.Lq) return;
-  if (a.n_splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T* og = reinterpret_cast<T*>(a.out) + ((size_t)bh * a.Lq + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = 32 * db + 8 * g + 4 * hh;
-        if constexpr (BF) {
-          f32x2 x0 = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv};
-          f32x2 x1 = {o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-          bf16x2 y0 = __builtin_convertvector(x0, bf16x2), y1 = __builtin_convertvector(x1, bf16x2);
-          bf16x4 y = {y0[0], y0[1], y1[0], y1[1]};
-          *reinterpret_cast<bf16x4*>(og + dd) = y;
-        } else {
-          f32x4 y = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(og + dd) = y;
+        for (int g = 0; g < 4; ++g) {
+          const int dd = 32 * db + 8 * g + 4 * hh;
+          if constexpr (BF) {
+            const bf16x2 y0 = cvt2(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv);
+            const bf16x2 y1 = cvt2(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
+            const bf16x4 y = {y0[0], y0[1], y1[0], y1[1]};
+            *reinterpret_cast<bf16x4*>(og + dd) = y;
+          } else {
+            const f32x4 y = {o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv,
+                             o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(og + dd) = y;
+          }
         }
-      }
-  } else {
-    const size_t row = ((size_t)split * a.B * a.H + bh) * a.Lq + qrow;
-    float* po = a.part_o + row * D;
+    } else {
+      const size_t row = ((size_t)split * a.B * a.H + bh) * a.Lq + qrow[qb];
+      float* po = a.part_o + row * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = 32 * db + 8 * g + 4 * hh;
-        f32x4 y = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(po + dd) = y;
+        for (int g = 0; g < 4; ++g) {
+          const int dd = 32 * db + 8 * g + 4 * hh;
+          const f32x4 y = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2], o[qb][db][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(po + dd) = y;
+        }
+      if (hh == 0) {
+        const f32x2 ml = {l_tot > 0.f ? m_use * c : RA_NEG_INF, l_tot};
+        *reinterpret_cast<f32x2*>(a.part_ml + row * 2) = ml;
       }
-    if (hh == 0) {
-      f32x2 ml = {l_tot > 0.f ? m_use * c : RA_NEG_INF, l_tot};
-      *reinterpret_cast<f32x2*>(a.part_ml + row * 2) = ml;
     }
   }
 }
@@ -726,17 +927,16 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   T* og = reinterpret_cast<T*>(a.out) + row * D + 4 * ch;
   if constexpr (BF) {
-    f32x2 x0 = {acc[0] * inv, acc[1] * inv}, x1 = {acc[2] * inv, acc[3] * inv};
-    bf16x2 y0 = __builtin_convertvector(x0, bf16x2), y1 = __builtin_convertvector(x1, bf16x2);
-    bf16x4 y = {y0[0], y0[1], y1[0], y1[1]};
+    const bf16x2 y0 = cvt2(acc[0] * inv, acc[1] * inv), y1 = cvt2(acc[2] * inv, acc[3] * inv);
+    const bf16x4 y = {y0[0], y0[1], y1[0], y1[1]};
     *reinterpret_cast<bf16x4*>(og) = y;
   } else {
-    f32x4 y = acc * inv;
+    const f32x4 y = acc * inv;
     *reinterpret_cast<f32x4*>(og) = y;
   }
 }
 
-// DeBERTa per-key constants for tiles whose offsets are all clipped:
+// DeBERTa per-key constants for blocks whose offsets are all clipped:
 // colc[0][bh][j] = k_j . Qr[0][h] (key far before the query: d(j,i) = 0),
 // colc[1][bh][j] = k_j . Qr[2k-1][h] (key far after it).  Keys in the
 // padding up to Lk_pad get 0.
@@ -768,22 +968,35 @@ __global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
 // Host-side launch helpers (called from relattn_api.cpp)
 // ----------------------------------------------------------------------------
 
-template <int KIND, bool BF, int D>
+template <int KIND, bool BF, int D, int QB, int NW>
 static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t st) {
-  auto kfn = relattn_fwd_kernel<KIND, BF, D>;
+  auto kfn = relattn_fwd_kernel<KIND, BF, D, QB, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kfn, dim3(grid), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL(kfn, dim3(grid), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(int kind, bool bf, int d, const FwdArgs& a, int grid, int lds, hipStream_t st) {
-#define RA_CASE(K, B, DD) \
-  if (kind == K && bf == B && d == DD) return launch_fwd_t<K, B, DD>(a, grid, lds, st);
-  RA_CASE(0, true, 64) RA_CASE(0, true, 32) RA_CASE(0, false, 64) RA_CASE(0, false, 32)
-  RA_CASE(1, true, 64) RA_CASE(1, true, 32) RA_CASE(1, false, 64) RA_CASE(1, false, 32)
-  RA_CASE(2, true, 64) RA_CASE(2, true, 32) RA_CASE(2, false, 64) RA_CASE(2, false, 32)
+bool fwd_variant_built(int kind, bool bf, Variant v) {
+  if (kind == 2) return v.qb == 1 && v.nw == (bf ? 8 : 4);
+  return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
+}
+
+hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int grid, int lds,
+                      hipStream_t st) {
+#define RA_CASE(K, B, DD, QBV, NWV)                                     \
+  if (kind == K && bf == B && d == DD && v.qb == QBV && v.nw == NWV) \
+    return launch_fwd_t<K, B, DD, QBV, NWV>(a, grid, lds, st);
+#define RA_DT(K, QBV, NWV)                                                        \
+  RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
+  RA_CASE(K, false, 32, QBV, NWV)
+  RA_DT(0, 1, 4) RA_DT(1, 1, 4)
+  RA_CASE(2, true, 64, 1, 8) RA_CASE(2, true, 32, 1, 8)
+  RA_CASE(2, false, 64, 1, 4) RA_CASE(2, false, 32, 1, 4)
+  RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
+  RA_CASE(1, true, 64, 2, 4) RA_CASE(1, true, 32, 2, 4)
+#undef RA_DT
 #undef RA_CASE
   return hipErrorInvalidValue;
 }
