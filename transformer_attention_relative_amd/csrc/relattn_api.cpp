@@ -173,6 +173,12 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   }
   relattn_status ls = lds_for(var, &lds_total, &lut_n);
   if (ls != RELATTN_OK) return ls;
+  if (lds_total > kLdsPerCU && p->kind == RELATTN_SHAW && !P->bf) {
+    // float32 Shaw with a wide clip window: two waves per workgroup
+    var = Variant{2, 1};
+    ls = lds_for(var, &lds_total, &lut_n);
+    if (ls != RELATTN_OK) return ls;
+  }
   if (!fwd_variant_built(p->kind, P->bf, var)) return fail(RELATTN_ERR_UNSUPPORTED, "no kernel variant");
   P->var = var;
   const int BQ = kBlockRows * var.qb * var.nw;

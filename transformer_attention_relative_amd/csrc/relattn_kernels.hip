@@ -273,6 +273,19 @@ __device__ __forceinline__ float load_v_f32(const char* vtile, int key, int dd) 
                                          (dd & 3) * 4);
 }
 
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
+// writes LDS bytes lds_base + 16*l .. +15; lds_base must be wave-uniform.
+// Issued through inline asm so that the compiler does not treat the copy as
+// a pending LDS store that every later LDS read must wait for; the kernel
+// orders it itself (s_waitcnt vmcnt + a workgroup barrier before any read).
+__device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const RA_LDS char*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(m0)
+               : "memory", "m0");
+}
+
 // Issue the direct global -> LDS loads of one K tile and one V tile.
 // Instruction `ins` of a tile covers rows ins*RPI .. +RPI-1; lane l fills LDS
 // slot l of that 1 KiB block: row ins*RPI + l/CPR, slot l%CPR, which holds
@@ -292,8 +305,8 @@ __device__ __forceinline__ void issue_tile(const char* Kg, const char* Vg, int L
       const int chunk = slot ^ (row & SWZ);
       const int grow = min(k0 + row, Lk - 1);
       const size_t goff = (size_t)grow * (D * ESZ) + chunk * 16;
-      __builtin_amdgcn_global_load_lds(Kg + goff, (RA_LDS void*)(stage + ins * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vg + goff, (RA_LDS void*)(stage + tile_bytes + ins * 1024), 16, 0, 0);
+      lds_dma16(Kg + goff, stage + ins * 1024);
+      lds_dma16(Vg + goff, stage + tile_bytes + ins * 1024);
     }
   }
 }
