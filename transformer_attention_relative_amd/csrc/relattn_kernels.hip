@@ -157,9 +157,32 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
   return acc;
 }
 
+// max(x[l], x[l ^ 32]) in every lane l without going through LDS:
+// v_permlane32_swap on (x, x) exchanges the high half of the first copy with
+// the low half of the second, so one result holds the low half's values in
+// both halves and the other the high half's.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // In the 32x32 accumulator layout, register i of a lane in half hh holds
 // row 8*(i/4) + 4*hh + (i%4) of the lane's column.
 __device__ __forceinline__ int acc_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+// Slot permutation of LDS tile rows: chunk c of row r (CPR 16-byte chunks per
+// row) is stored in slot c ^ swz<CPR>(r).  The masks are GF(2)-linear in the
+// row bits, chosen so that the K fragment reads (16 or 32 consecutive lanes
+// reading 16 bytes from consecutive rows) and the V transpose reads (32 or 64
+// lanes reading 8 bytes from 4 or 8 consecutive rows, 4 chunks each) touch
+// every LDS bank once per cycle whether a cycle serves 256 or 512 bytes.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 4) return (((r >> 2) ^ (r >> 4)) & 1) | (((r >> 3) & 1) << 1);
+  else if constexpr (CPR == 8)
+    return ((r >> 3) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 2) ^ (r >> 4)) & 1) << 2);
+  else return ((r ^ (r >> 4)) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2) | (((r >> 1) & 1) << 3);
+}
 
 // A row-major table row as an MFMA operand (A row or B column): bf16 chunk t
 // holds elements 16t + 8hh .. +7; fp32 element t is d-index t + (d/2)*hh.
@@ -174,11 +197,12 @@ struct TableFrag<true, D> {
   }
   // row `r` of a swizzled LDS tile (see relattn_internal.hpp)
   __device__ __forceinline__ void load_lds(const char* tile, int r, int hh) {
-    constexpr int CPR = D / 8, SWZ = (CPR < 8 ? CPR : 8) - 1;
+    constexpr int CPR = D / 8;
     const char* rp = tile + r * CPR * 16;
+    const int sw = swz<CPR>(r);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      v[t] = *reinterpret_cast<const bf16x8*>(rp + (((2 * t + hh) ^ (r & SWZ)) * 16));
+      v[t] = *reinterpret_cast<const bf16x8*>(rp + (((2 * t + hh) ^ sw) * 16));
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -196,11 +220,12 @@ struct TableFrag<false, D> {
     }
   }
   __device__ __forceinline__ void load_lds(const char* tile, int r, int hh) {
-    constexpr int CPR = D / 4, SWZ = (CPR < 8 ? CPR : 8) - 1;
+    constexpr int CPR = D / 4;
     const char* rp = tile + r * CPR * 16;
+    const int sw = swz<CPR>(r);
 #pragma unroll
     for (int t = 0; t < D / 8; ++t) {
-      f32x4 x = *reinterpret_cast<const f32x4*>(rp + ((((D / 8) * hh + t) ^ (r & SWZ)) * 16));
+      f32x4 x = *reinterpret_cast<const f32x4*>(rp + ((((D / 8) * hh + t) ^ sw) * 16));
       v[4 * t + 0] = x[0]; v[4 * t + 1] = x[1]; v[4 * t + 2] = x[2]; v[4 * t + 3] = x[3];
     }
   }
@@ -249,14 +274,14 @@ __device__ __forceinline__ f32x16 mma_frag(const TableFrag<BF, D>& a, const Tabl
 // 32db + lane%32 -- the same key order as P in the score accumulator.
 template <int D>
 __device__ __forceinline__ bf16x8 load_vt_frag(const char* vtile, int cc, int db, int lane) {
-  constexpr int CPR = D / 8, SWZ = (CPR < 8 ? CPR : 8) - 1;
+  constexpr int CPR = D / 8;
   const int G = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
   const int c = 4 * db + 2 * (G & 1) + (j >> 1);
   i16x4 r[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int key = 16 * cc + 8 * half + 4 * (G >> 1) + e;
-    const char* addr = vtile + key * CPR * 16 + ((c ^ (key & SWZ)) * 16) + 8 * (j & 1);
+    const char* addr = vtile + key * CPR * 16 + ((c ^ swz<CPR>(key)) * 16) + 8 * (j & 1);
     r[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(addr));
   }
   const i16x4 lo = r[0], hi = r[1];
@@ -268,8 +293,8 @@ __device__ __forceinline__ bf16x8 load_vt_frag(const char* vtile, int cc, int db
 // float32 V element (key, head dim) of the swizzled row-major tile.
 template <int D>
 __device__ __forceinline__ float load_v_f32(const char* vtile, int key, int dd) {
-  constexpr int CPR = D / 4, SWZ = (CPR < 8 ? CPR : 8) - 1;
-  return *reinterpret_cast<const float*>(vtile + key * CPR * 16 + (((dd >> 2) ^ (key & SWZ)) * 16) +
+  constexpr int CPR = D / 4;
+  return *reinterpret_cast<const float*>(vtile + key * CPR * 16 + (((dd >> 2) ^ swz<CPR>(key)) * 16) +
                                          (dd & 3) * 4);
 }
 
@@ -289,12 +314,12 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds_base
 // Issue the direct global -> LDS loads of one K tile and one V tile.
 // Instruction `ins` of a tile covers rows ins*RPI .. +RPI-1; lane l fills LDS
 // slot l of that 1 KiB block: row ins*RPI + l/CPR, slot l%CPR, which holds
-// chunk slot ^ (row & SWZ).  Rows past the end of the keys re-read the last
+// chunk slot ^ swz(row).  Rows past the end of the keys re-read the last
 // key (in bounds; those keys are masked).
 template <bool BF, int D, int NW>
 __device__ __forceinline__ void issue_tile(const char* Kg, const char* Vg, int Lk, int k0,
                                            char* stage, int tile_bytes, int wave, int lane) {
-  constexpr int ESZ = BF ? 2 : 4, CPR = D * ESZ / 16, SWZ = (CPR < 8 ? CPR : 8) - 1;
+  constexpr int ESZ = BF ? 2 : 4, CPR = D * ESZ / 16;
   constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
 #pragma unroll
   for (int r = 0; r < IPW; ++r) {
@@ -302,7 +327,7 @@ __device__ __forceinline__ void issue_tile(const char* Kg, const char* Vg, int L
     if (ins < IPT) {
       const int row = ins * RPI + lane / CPR;
       const int slot = lane % CPR;
-      const int chunk = slot ^ (row & SWZ);
+      const int chunk = slot ^ swz<CPR>(row);
       const int grow = min(k0 + row, Lk - 1);
       const size_t goff = (size_t)grow * (D * ESZ) + chunk * 16;
       lds_dma16(Kg + goff, stage + ins * 1024);
@@ -332,15 +357,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   const LdsLayout L = lds_layout(KIND, BF, D, QB, NW, a.clip_k, a.lut_n);
   float* relf = reinterpret_cast<float*>(smem + L.rel_off);
 
-  // ---- work item (XCD-aware: consecutive logical ids share an L2) ----------
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
-  const int lid = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
-  const int per_bh = a.n_qtiles * a.n_splits;
-  const int bh = lid / per_bh;
-  const int rest = lid - bh * per_bh;
-  const int qt = a.n_qtiles - 1 - rest / a.n_splits;  // heavy (late) tiles first
-  const int split = rest % a.n_splits;
+  // ---- work item -------------------------------------------------------------
+  // Workgroups are dispatched in id order, round-robin over the 8 XCDs.  The
+  // query-tile rank is the major index, heaviest (latest causal) tiles first,
+  // so every XCD starts its longest items first; (head, split) is the minor
+  // index, so when B*H*splits is a multiple of 8 every item of one (head,
+  // split) lands on the same XCD and shares its L2.
+  const int per_rank = a.B * a.H * a.n_splits;
+  const int rank = blockIdx.x / per_rank;
+  const int rest = blockIdx.x - rank * per_rank;
+  const int bh = rest / a.n_splits;
+  const int split = rest - bh * a.n_splits;
+  const int qt = a.n_qtiles - 1 - rank;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
 
   const int tid = threadIdx.x;
@@ -736,7 +764,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_halves(mx);
       const float cand = mx + b_raw[qb];
       const bool need = cand > m_run[qb] + thr_raw;
       if (__any(need)) {
