@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 instructions stay off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaNs in the kernels' arithmetic (scores are finite or -inf): fmaxf
+    # then maps to v_max / v_max3 without quieting each operand first
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

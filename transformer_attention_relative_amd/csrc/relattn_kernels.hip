@@ -157,31 +157,64 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
   return acc;
 }
 
+// max of three (v_max3_f32).  The library is compiled without NaN support
+// (-fno-honor-nans): scores are finite or -inf, and with NaNs possible every
+// fmaxf operand would first be quieted by an extra v_max.
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Max of the 16 scores a lane holds for one 32-key block (two chains).
+__device__ __forceinline__ float max16(const f32x16& x) {
+  float m0 = vmax3(x[0], x[1], x[2]), m1 = vmax3(x[3], x[4], x[5]);
+  m0 = vmax3(m0, x[6], x[7]);
+  m1 = vmax3(m1, x[8], x[9]);
+  m0 = vmax3(m0, x[10], x[11]);
+  m1 = vmax3(m1, x[12], x[13]);
+  return vmax3(m0, m1, vmax3(x[14], x[15], x[15]));
+}
+
+// The lane index, computed by instructions the compiler may not move: values
+// derived from it inside a loop stay inside that loop instead of being
+// hoisted (and kept live) across the whole kernel.
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // max(x[l], x[l ^ 32]) in every lane l without going through LDS:
 // v_permlane32_swap on (x, x) exchanges the high half of the first copy with
 // the low half of the second, so one result holds the low half's values in
 // both halves and the other the high half's.
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+  return vmax3(lo, hi, hi);
 }
 
 // In the 32x32 accumulator layout, register i of a lane in half hh holds
 // row 8*(i/4) + 4*hh + (i%4) of the lane's column.
 __device__ __forceinline__ int acc_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
 
-// Slot permutation of LDS tile rows: chunk c of row r (CPR 16-byte chunks per
-// row) is stored in slot c ^ swz<CPR>(r).  The masks are GF(2)-linear in the
-// row bits, chosen so that the K fragment reads (16 or 32 consecutive lanes
-// reading 16 bytes from consecutive rows) and the V transpose reads (32 or 64
-// lanes reading 8 bytes from 4 or 8 consecutive rows, 4 chunks each) touch
-// every LDS bank once per cycle whether a cycle serves 256 or 512 bytes.
+// Slot permutations of the LDS tile rows: chunk c of K row r (CPR 16-byte
+// chunks per row) is stored in slot c ^ swz_k<CPR>(r), chunk c of V row r in
+// slot c ^ swz_v<CPR>(r).  The masks are GF(2)-linear in the row bits.
+// swz_k: the K fragment reads (16 or 32 consecutive lanes reading 16 bytes
+// from consecutive rows) touch every bank once per cycle whether a cycle
+// serves 256 or 512 bytes.  swz_v: the V transpose reads (32 or 64 lanes
+// reading 8 bytes from 4 or 8 consecutive rows) do the same, and the mask
+// depends on the row's low 3 bits only, so every V read of a tile is one
+// per-lane offset plus an immediate.
 template <int CPR>
-__device__ __forceinline__ int swz(int r) {
+__device__ __forceinline__ int swz_k(int r) {
   if constexpr (CPR == 4) return (((r >> 2) ^ (r >> 4)) & 1) | (((r >> 3) & 1) << 1);
   else if constexpr (CPR == 8)
     return ((r >> 3) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 2) ^ (r >> 4)) & 1) << 2);
   else return ((r ^ (r >> 4)) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2) | (((r >> 1) & 1) << 3);
+}
+template <int CPR, bool BF>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (BF && CPR == 8) return (((r >> 1) ^ (r >> 2)) & 1) << 2;
+  else return 0;
 }
 
 // A row-major table row as an MFMA operand (A row or B column): bf16 chunk t
@@ -195,14 +228,10 @@ struct TableFrag<true, D> {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) v[t] = *reinterpret_cast<const bf16x8*>(row + 16 * t + 8 * hh);
   }
-  // row `r` of a swizzled LDS tile (see relattn_internal.hpp)
-  __device__ __forceinline__ void load_lds(const char* tile, int r, int hh) {
-    constexpr int CPR = D / 8;
-    const char* rp = tile + r * CPR * 16;
-    const int sw = swz<CPR>(r);
+  // a row of a swizzled LDS K tile; off[t] = byte offset of chunk t (see KOffsets)
+  __device__ __forceinline__ void load_lds(const char* base, const int* off) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      v[t] = *reinterpret_cast<const bf16x8*>(rp + (((2 * t + hh) ^ sw) * 16));
+    for (int t = 0; t < D / 16; ++t) v[t] = *reinterpret_cast<const bf16x8*>(base + off[t]);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -219,13 +248,10 @@ struct TableFrag<false, D> {
       v[4 * t + 0] = x[0]; v[4 * t + 1] = x[1]; v[4 * t + 2] = x[2]; v[4 * t + 3] = x[3];
     }
   }
-  __device__ __forceinline__ void load_lds(const char* tile, int r, int hh) {
-    constexpr int CPR = D / 4;
-    const char* rp = tile + r * CPR * 16;
-    const int sw = swz<CPR>(r);
+  __device__ __forceinline__ void load_lds(const char* base, const int* off) {
 #pragma unroll
     for (int t = 0; t < D / 8; ++t) {
-      f32x4 x = *reinterpret_cast<const f32x4*>(rp + ((((D / 8) * hh + t) ^ sw) * 16));
+      f32x4 x = *reinterpret_cast<const f32x4*>(base + off[t]);
       v[4 * t + 0] = x[0]; v[4 * t + 1] = x[1]; v[4 * t + 2] = x[2]; v[4 * t + 3] = x[3];
     }
   }
@@ -264,38 +290,63 @@ __device__ __forceinline__ f32x16 mma_frag(const TableFrag<BF, D>& a, const Tabl
   return c;
 }
 
-// V^T fragment (A operand of O^T = V^T P^T) for the 16-key chunk cc and the
-// 32-wide head-dim block db, read from the row-major swizzled V tile with the
-// LDS transpose read.  ds_read_b64_tr_b16 gives lane (group G = lane/16,
-// index i) the elements e = 0..3 of the 8-byte chunks addressed by lanes
-// 16G + 4e + i/4, each at position i%4.  So lane (G, e, j) addresses key
-// 16cc + 8*half + 4*(G/2) + e at head dims 32db + 16*(G%2) + 4j .. +3, and
-// every lane receives the 4 keys of its MFMA k-slots at head dim
-// 32db + lane%32 -- the same key order as P in the score accumulator.
-template <int D>
-__device__ __forceinline__ bf16x8 load_vt_frag(const char* vtile, int cc, int db, int lane) {
-  constexpr int CPR = D / 8;
-  const int G = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
-  const int c = 4 * db + 2 * (G & 1) + (j >> 1);
-  i16x4 r[2];
+// Per-lane byte offsets into the K and V tiles, fixed for the whole key loop
+// (a tile read is its stage base + one of these + an immediate).
+//   k[t]: the 16-byte chunk t of the lane's K fragment row lq (the MFMA A
+//         row) of a 32-key block; bf16 chunk t holds head dims 16t + 8hh ..,
+//         float32 chunk t holds head dims 4t + (d/2)hh ..
+//   v[db] (bf16): the V^T fragment (A operand of O^T = V^T P^T) for head-dim
+//         block db, read with ds_read_b64_tr_b16.  The transpose read gives
+//         lane (group G = lane/16, index i) the elements e = 0..3 of the
+//         8-byte chunks addressed by lanes 16G + 4e + i/4, each at position
+//         i%4.  So lane (G, e, j) addresses key 16cc + 8*half + 4*(G/2) + e
+//         at head dims 32db + 16*(G%2) + 4j .. +3, and every lane receives
+//         the 4 keys of its MFMA k-slots at head dim 32db + lane%32 -- the
+//         same key order as P in the score accumulator.
+//   v[0] (float32): key 4hh + (cc%4) + 8(cc/4) of a 32-key block at head dim
+//         lq (plus 32db and the key offsets as immediates).
+template <bool BF, int D>
+struct KOffsets {
+  static constexpr int ESZ = BF ? 2 : 4, ROWB = D * ESZ, CPR = ROWB / 16;
+  static constexpr int NK = BF ? D / 16 : D / 8;
+  static constexpr int NV = BF ? D / 32 : 1;
+  int k[NK], v[NV];
+  __device__ __forceinline__ void init(int lane) {
+    const int lq = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int key = 16 * cc + 8 * half + 4 * (G >> 1) + e;
-    const char* addr = vtile + key * CPR * 16 + ((c ^ swz<CPR>(key)) * 16) + 8 * (j & 1);
-    r[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(addr));
+    for (int t = 0; t < NK; ++t) {
+      const int chunk = BF ? 2 * t + hh : (D / 8) * hh + t;
+      k[t] = lq * ROWB + ((chunk ^ swz_k<CPR>(lq)) * 16);
+    }
+    if constexpr (BF) {
+      const int G = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
+      const int kl = 4 * (G >> 1) + e;
+#pragma unroll
+      for (int db = 0; db < NV; ++db) {
+        const int c = 4 * db + 2 * (G & 1) + (j >> 1);
+        v[db] = kl * ROWB + ((c ^ swz_v<CPR, BF>(kl)) * 16) + 8 * (j & 1);
+      }
+    } else {
+      v[0] = 4 * hh * ROWB + lq * 4;
+    }
   }
-  const i16x4 lo = r[0], hi = r[1];
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 load_vt_frag(const char* vtile, int cc, const int vo) {
+  constexpr int ROWB = D * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vtile + vo + (16 * cc) * ROWB));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vtile + vo + (16 * cc + 8) * ROWB));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// float32 V element (key, head dim) of the swizzled row-major tile.
+// float32 V element: key 32kb + acc_row(cc, hh), head dim 32db + lq.
 template <int D>
-__device__ __forceinline__ float load_v_f32(const char* vtile, int key, int dd) {
-  constexpr int CPR = D / 4;
-  return *reinterpret_cast<const float*>(vtile + key * CPR * 16 + (((dd >> 2) ^ swz<CPR>(key)) * 16) +
-                                         (dd & 3) * 4);
+__device__ __forceinline__ float load_v_f32(const char* vtile, int kb, int cc, int db, const int vo) {
+  constexpr int ROWB = D * 4;
+  return *reinterpret_cast<const float*>(vtile + vo + (32 * kb + 8 * (cc >> 2) + (cc & 3)) * ROWB + 128 * db);
 }
 
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
@@ -311,30 +362,64 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds_base
                : "memory", "m0");
 }
 
-// Issue the direct global -> LDS loads of one K tile and one V tile.
-// Instruction `ins` of a tile covers rows ins*RPI .. +RPI-1; lane l fills LDS
-// slot l of that 1 KiB block: row ins*RPI + l/CPR, slot l%CPR, which holds
-// chunk slot ^ swz(row).  Rows past the end of the keys re-read the last
-// key (in bounds; those keys are masked).
+// Same copy with a wave-uniform 64-bit global base and a per-lane 32-bit
+// offset (the scalar-base form: the per-tile address update is scalar).
+__device__ __forceinline__ void lds_dma16_s(const char* gbase, int goff, const char* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const RA_LDS char*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(goff), "s"(gbase), "s"(m0)
+               : "memory", "m0");
+}
+
+// Direct global -> LDS loads of one K tile and one V tile.  Instruction `ins`
+// of a tile covers rows ins*RPI .. +RPI-1; lane l fills LDS slot l of that
+// 1 KiB block: row ins*RPI + l/CPR, slot l%CPR, which holds chunk
+// slot ^ swz(row).  The per-lane offsets are fixed; a tile that runs past
+// the last key re-reads the last key for those rows (in bounds; the keys are
+// masked).
 template <bool BF, int D, int NW>
-__device__ __forceinline__ void issue_tile(const char* Kg, const char* Vg, int Lk, int k0,
-                                           char* stage, int tile_bytes, int wave, int lane) {
-  constexpr int ESZ = BF ? 2 : 4, CPR = D * ESZ / 16;
-  constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
+struct TileDma {
+  static constexpr int ESZ = BF ? 2 : 4, ROWB = D * ESZ, CPR = ROWB / 16;
+  static constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
+  static constexpr int LPW = 2 * IPW;  // load instructions per wave per tile
+  int ko[IPW], vo[IPW];
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int r = 0; r < IPW; ++r) {
-    const int ins = wave + r * NW;
-    if (ins < IPT) {
-      const int row = ins * RPI + lane / CPR;
-      const int slot = lane % CPR;
-      const int chunk = slot ^ swz<CPR>(row);
-      const int grow = min(k0 + row, Lk - 1);
-      const size_t goff = (size_t)grow * (D * ESZ) + chunk * 16;
-      lds_dma16(Kg + goff, stage + ins * 1024);
-      lds_dma16(Vg + goff, stage + tile_bytes + ins * 1024);
+    for (int r = 0; r < IPW; ++r) {
+      const int row = (wave + r * NW) * RPI + lane / CPR, slot = lane % CPR;
+      ko[r] = row * ROWB + ((slot ^ swz_k<CPR>(row)) * 16);
+      vo[r] = row * ROWB + ((slot ^ swz_v<CPR, BF>(row)) * 16);
     }
   }
-}
+  __device__ __forceinline__ void issue(const char* Kg, const char* Vg, int Lk, int k0, char* stage,
+                                        int tile_bytes, int wave, int lane) const {
+    if (k0 + kBK <= Lk) {
+      const char* kb = Kg + (size_t)k0 * ROWB;
+      const char* vb = Vg + (size_t)k0 * ROWB;
+#pragma unroll
+      for (int r = 0; r < IPW; ++r) {
+        const int ins = wave + r * NW;
+        if (ins < IPT) {
+          lds_dma16_s(kb, ko[r], stage + ins * 1024);
+          lds_dma16_s(vb, vo[r], stage + tile_bytes + ins * 1024);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < IPW; ++r) {
+        const int ins = wave + r * NW;
+        if (ins < IPT) {
+          const int row = ins * RPI + lane / CPR;
+          const int grow = min(k0 + row, Lk - 1);
+          const long long shift = (long long)(grow - row) * ROWB;  // may be negative
+          lds_dma16(Kg + shift + ko[r], stage + ins * 1024);
+          lds_dma16(Vg + shift + vo[r], stage + tile_bytes + ins * 1024);
+        }
+      }
+    }
+  }
+};
 
 // ----------------------------------------------------------------------------
 // The fused forward kernel
@@ -342,16 +427,17 @@ __device__ __forceinline__ void issue_tile(const char* Kg, const char* Vg, int L
 
 template <int KIND, bool BF, int D, int QB, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a) {
+  static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
   using T = typename std::conditional<BF, bf16, float>::type;
   constexpr int NKB = kBK / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
   constexpr int RW = 32 * QB;         // query rows per wave
   constexpr int BQ = RW * NW;         // query rows per workgroup
   constexpr int NS = num_stages(KIND, BF);
-  constexpr int ESZ = BF ? 2 : 4, CPR = D * ESZ / 16;
-  constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
-  constexpr int LPW = 2 * IPW;        // load instructions per wave per tile
-  constexpr bool EVEN_LOADS = (IPT % NW) == 0;
+  using Dma = TileDma<BF, D, NW>;
+  constexpr int ROWB = Dma::ROWB;     // bytes per K / V row
+  constexpr int LPW = Dma::LPW;       // load instructions per wave per tile
+  constexpr bool EVEN_LOADS = (Dma::IPT % NW) == 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const LdsLayout L = lds_layout(KIND, BF, D, QB, NW, a.clip_k, a.lut_n);
@@ -458,6 +544,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   }
 
   // ---- start streaming the first key tiles --------------------------------
+  Dma dma;
+  dma.init(wave, lane);
   // Without a key split the first tiles are known before the valid length is
   // read (tiles past it are loaded in bounds and never used).
   const int reach0 = a.causal ? min(a.Lk, wg_pos_max + 1) : a.Lk;
@@ -465,7 +553,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < n_pre0)
-      issue_tile<BF, D, NW>(Kg, Vg, a.Lk, s * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
+      dma.issue(Kg, Vg, a.Lk, s * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
 
   int kv_lim = a.Lk;
   if (a.kv_valid_len) kv_lim = max(0, min(kv_lim, a.kv_valid_len[b]));
@@ -479,8 +567,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < n_my)
-        issue_tile<BF, D, NW>(Kg, Vg, a.Lk, (kt_begin + s) * kBK, smem + s * L.stage_bytes,
-                              L.tile_bytes, wave, lane);
+        dma.issue(Kg, Vg, a.Lk, (kt_begin + s) * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
   }
 
   // ---- per-kind prologue (LDS tables) ---------------------------------------
@@ -568,7 +655,47 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     win_run[qb] = 0.f;       // Shaw: partial mass of keys inside the clip window
   }
 
-  for (int r = 0; r < n_my; ++r) {
+  // Tile classes (wave-uniform):
+  //   0: every block far from the diagonal band (the relative term is a
+  //      per-row constant, or a per-key constant for DeBERTa), no mask;
+  //   1: T5, every block inside the bucket table's range, no mask;
+  //   2: anything else (band terms, masks, Shaw bins);
+  //   3: nothing to do for this wave (past its causal reach).
+  // Runs of equal class go through a loop of their own, so the lean loops
+  // are not burdened with the registers of the general one.
+  auto tile_class = [&](const int r) -> int {
+    const int k0 = (kt_begin + r) * kBK;
+    if (!wave_active || (a.causal && k0 > pw_max_real)) return 3;
+    bool far_all = true, near_all = true;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
+      const int omin = k0 - pq_max, omax = k0 + kBK - 1 - pq_min;  // key - query
+      bool far;
+      if constexpr (KIND == 0) far = omax <= -a.t5_lsat || omin >= a.t5_rsat;
+      else if constexpr (KIND == 1) far = omin >= ck || omax <= -ck;
+      else far = -omax >= ck || -omin <= -ck;
+      far_all = far_all && far;
+      near_all = near_all && !far;
+    }
+    // no block of the tile touches the causal diagonal or the end of the keys
+    const bool unmasked = !(a.causal && k0 + kBK - 1 > pw_min) && (k0 + kBK <= kv_lim);
+    if (unmasked && far_all) return 0;
+    if (KIND == 0 && unmasked && near_all) return 1;
+    return 2;
+  };
+
+  auto run_tile = [&](auto cls_tag, const int r, const int ln) {
+    constexpr int CLS = decltype(cls_tag)::value;
+    // per-lane values, from the loop's own lane index (see opaque_lane)
+    const int lane = ln, lq = ln & 31, hh = ln >> 5;
+    int pos[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) pos[qb] = pw_min + 32 * qb + lq;
+    KOffsets<BF, D> ko;
+    ko.init(lane);
+    Dma dma;
+    dma.init(wave, lane);
     const int kt = kt_begin + r;
     if constexpr (NS >= 3 && EVEN_LOADS) {
       // tiles newer than r that may still be in flight: min(NS - 2, n_my - 1 - r)
@@ -581,12 +708,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     }
     __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     const int k0 = kt * kBK;
-    const bool active = wave_active && !(a.causal && k0 > pw_max_real);
     // DeBERTa per-key constants of clipped blocks are requested before the
     // next tiles, so waiting for them never waits for the prefetch
     f32x4 colv[QB][NKB][4];
     if constexpr (KIND == 2) {
-      if (active) {
+      if (CLS != 3) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -603,13 +729,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       }
     }
     if (r + NS - 1 < n_my)
-      issue_tile<BF, D, NW>(Kg, Vg, a.Lk, (kt + NS - 1) * kBK, smem + ((r + NS - 1) % NS) * L.stage_bytes,
-                            L.tile_bytes, wave, lane);
+      dma.issue(Kg, Vg, a.Lk, (kt + NS - 1) * kBK, smem + ((r + NS - 1) % NS) * L.stage_bytes,
+                L.tile_bytes, wave, lane);
+    if constexpr (CLS == 3) return;
     const char* ktile = smem + (r % NS) * L.stage_bytes;
     const char* vtile = ktile + L.tile_bytes;
-    if (!active) continue;
 
-    f32x16 s[QB][NKB];
+    // ---- the tile's query blocks (wave-uniform) ----
     float b_raw[QB];
     bool near[QB], far_right[QB];
     int deb_side[QB];  // DeBERTa: 0 far-left tile, 1 far-right tile, -1 mixed
@@ -644,179 +770,198 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       }
     }
 
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    // One step of 32 keys (block kb of the tile) for the query blocks in the
+    // bit mask QM: scores, online softmax, P V.  A K fragment and a V fragment
+    // read from LDS feed every query block of the step.  Class 2 runs one
+    // query block per step so that fewer values are live.
+    auto step = [&](auto qm_tag, const int kb) {
+      constexpr int QM = decltype(qm_tag)::value;
       const int j0 = k0 + 32 * kb;
-      TableFrag<BF, D> kf;
-      kf.load_lds(ktile, 32 * kb + lq, hh);
+      f32x16 s[QB];
+      {
+        TableFrag<BF, D> kf;
+        kf.load_lds(ktile + 32 * kb * ROWB, ko.k);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
-        // (1)+(2) relative term into the accumulator, then S^T += K Q^T on top
-        // (far blocks start from the MFMA's zero accumulator input)
-        if constexpr (KIND == 0) {
-          if (near[qb]) {
-            f32x16 init;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 x = *reinterpret_cast<const f32x4*>(lutp[qb] + 32 * kb + 8 * g + 4 * hh);
-              init[4 * g + 0] = x[0]; init[4 * g + 1] = x[1];
-              init[4 * g + 2] = x[2]; init[4 * g + 3] = x[3];
-            }
-            s[qb][kb] = mma_frag<BF, D>(kf, qf[qb], init);
-          } else {
-            s[qb][kb] = mma_frag0<BF, D>(kf, qf[qb]);
-          }
-        } else if constexpr (KIND == 1) {
-          if (near[qb]) {
-            const float* ar = arel + (32 * qb + lq) * L.arel_stride;
-            f32x16 init;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) init[i] = ar[shaw_row_dev(j0 + acc_row(i, hh) - pos[qb], ck)];
-            s[qb][kb] = mma_frag<BF, D>(kf, qf[qb], init);
-          } else {
-            s[qb][kb] = mma_frag0<BF, D>(kf, qf[qb]);
-          }
-        } else {
-          const int tmin = pq_min - (j0 + 31), tmax = pq_max - j0;  // query - key over the block
-          int side = -1;
-          if (tmin >= ck) side = 0;
-          else if (tmax <= -ck) side = 1;
-          if (side >= 0) {
-            // per-key constant k_j.Qr[0] (side 0) or k_j.Qr[2k-1] (side 1); the
-            // per-row constant is folded into the exponent for whole-tile
-            // sides, else added here
-            const float add = deb_side[qb] >= 0 ? 0.f : (side == 0 ? crow_hi[qb] : crow_lo[qb]);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 x = colv[qb][kb][g];
-              s[qb][kb][4 * g + 0] = x[0] + add; s[qb][kb][4 * g + 1] = x[1] + add;
-              s[qb][kb][4 * g + 2] = x[2] + add; s[qb][kb][4 * g + 3] = x[3] + add;
-            }
-          } else {
-            float* cband = relf + wave * L.deb_wave_floats;
-            float* pband = cband + kBlockRows * kCbandStride;
-            const T* kr = reinterpret_cast<const T*>(a.table);
-            const T* qr = reinterpret_cast<const T*>(a.table2);
-            const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
-            // content-to-position: rows Kr[delta(T0 + m)], columns = queries
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-              TableFrag<BF, D> af;
-              af.load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
-              f32x16 acc = {};
-              acc = mma_frag<BF, D>(af, qf[qb], acc);
-              float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
+        for (int qb = 0; qb < QB; ++qb) {
+          if (!((QM >> qb) & 1)) continue;
+          const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
+          // (1)+(2) relative term into the accumulator, then S^T += K Q^T on top
+          // (far blocks start from the MFMA's zero accumulator input)
+          if constexpr (KIND == 0) {
+            if (CLS == 1 || (CLS == 2 && near[qb])) {
+              f32x16 init;
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
-                const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-                *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(lutp[qb] + 32 * kb + 8 * g + 4 * hh);
+                init[4 * g + 0] = x[0]; init[4 * g + 1] = x[1];
+                init[4 * g + 2] = x[2]; init[4 * g + 3] = x[3];
               }
+              s[qb] = mma_frag<BF, D>(kf, qf[qb], init);
+            } else {
+              s[qb] = mma_frag0<BF, D>(kf, qf[qb]);
             }
-            // position-to-content: rows = keys, columns n <-> query - key =
-            // T0 + n, Qr row delta(key - query); scattered to [query][key]
+          } else if constexpr (KIND == 1) {
+            if (CLS == 2 && near[qb]) {
+              const float* ar = arel + (32 * qb + lq) * L.arel_stride;
+              const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
+              f32x16 init;
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const int n = 32 * nb + lq;
-              TableFrag<BF, D> bfr;
-              bfr.load(qr + ((size_t)deberta_delta_dev(-(T0 + n), ck) * a.H + h) * D, hh);
-              f32x16 acc = {};
-              acc = mma_frag<BF, D>(kf, bfr, acc);
+              for (int i = 0; i < 16; ++i) init[i] = ar[shaw_row_dev(obase + acc_row(i, 0), ck)];
+              s[qb] = mma_frag<BF, D>(kf, qf[qb], init);
+            } else {
+              s[qb] = mma_frag0<BF, D>(kf, qf[qb]);
+            }
+          } else {
+            const int tmin = pq_min - (j0 + 31), tmax = pq_max - j0;  // query - key over the block
+            int side = -1;
+            if (tmin >= ck) side = 0;
+            else if (tmax <= -ck) side = 1;
+            if (CLS == 0 || side >= 0) {
+              // per-key constant k_j.Qr[0] (side 0) or k_j.Qr[2k-1] (side 1); the
+              // per-row constant is folded into the exponent for whole-tile
+              // sides, else added here
+              const float add = (CLS == 0 || deb_side[qb] >= 0) ? 0.f : (side == 0 ? crow_hi[qb] : crow_lo[qb]);
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int jl = acc_row(i, hh);
-                const int sq = n + jl - 31;
-                if (sq >= 0 && sq < 32) pband[sq * kPbandStride + jl] = acc[i];
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 x = colv[qb][kb][g];
+                s[qb][4 * g + 0] = x[0] + add; s[qb][4 * g + 1] = x[1] + add;
+                s[qb][4 * g + 2] = x[2] + add; s[qb][4 * g + 3] = x[3] + add;
               }
+            } else {
+              float* cband = relf + wave * L.deb_wave_floats;
+              float* pband = cband + kBlockRows * kCbandStride;
+              const T* kr = reinterpret_cast<const T*>(a.table);
+              const T* qr = reinterpret_cast<const T*>(a.table2);
+              const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
+              // content-to-position: rows Kr[delta(T0 + m)], columns = queries
+#pragma unroll
+              for (int tb = 0; tb < 2; ++tb) {
+                TableFrag<BF, D> af;
+                af.load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
+                const f32x16 acc = mma_frag0<BF, D>(af, qf[qb]);
+                float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+                  *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
+                }
+              }
+              // position-to-content: rows = keys, columns n <-> query - key =
+              // T0 + n, Qr row delta(key - query); scattered to [query][key]
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) {
+                const int n = 32 * nb + lq;
+                TableFrag<BF, D> bfr;
+                bfr.load(qr + ((size_t)deberta_delta_dev(-(T0 + n), ck) * a.H + h) * D, hh);
+                const f32x16 acc = mma_frag0<BF, D>(kf, bfr);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const int jl = acc_row(i, hh);
+                  const int sq = n + jl - 31;
+                  if (sq >= 0 && sq < 32) pband[sq * kPbandStride + jl] = acc[i];
+                }
+              }
+              wave_lds_fence();
+              const float* crow = cband + lq * kCbandStride + (pos[qb] - pq_min) + 31;
+              const float* prow = pband + lq * kPbandStride;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 pc = *reinterpret_cast<const f32x4*>(prow + 8 * g + 4 * hh);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[qb][4 * g + e] = crow[-(8 * g + 4 * hh + e)] + pc[e];
+              }
+              wave_lds_fence();  // the next block overwrites both bands
+            }
+            s[qb] = mma_frag<BF, D>(kf, qf[qb], s[qb]);
+          }
+          // (3) masks: hidden keys become -inf (only on blocks that touch the
+          // causal diagonal or the end of the valid keys)
+          if constexpr (CLS == 2) {
+            if ((a.causal && j0 + 31 > pq_min) || (j0 + 32 > kv_lim)) {
+              // register i holds key j0 + acc_row(i, hh) = j0 + 4hh + acc_row(i, 0);
+              // it is visible iff acc_row(i, 0) <= last - j0 - 4hh
+              const int last = a.causal ? min(kv_lim - 1, pos[qb]) : kv_lim - 1;
+              const int lim = last - j0 - 4 * hh;
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                if (acc_row(i, 0) > lim) s[qb][i] = RA_NEG_INF;
+            }
+          }
+        }
+      }
+
+      // (4) online softmax: row max (v_max3 pairs, then across the two lane
+      // halves); the reference max moves only when a block's max exceeds it
+      // by more than 2^8, for all query blocks of the step under one branch
+      float cand[QB];
+      bool need_any = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (!((QM >> qb) & 1)) continue;
+        cand[qb] = max_halves(max16(s[qb])) + b_raw[qb];
+        need_any = need_any || (cand[qb] > m_run[qb] + thr_raw);
+      }
+      if (__any(need_any)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          if (!((QM >> qb) & 1)) continue;
+          const bool need = cand[qb] > m_run[qb] + thr_raw;
+          const float m_new = need ? cand[qb] : m_run[qb];
+          const float alpha = fast_exp2((m_run[qb] - m_new) * c);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+          l_run[qb] *= alpha;
+          lr_run[qb] *= alpha;
+          win_run[qb] *= alpha;
+          m_run[qb] = m_new;
+        }
+      }
+      using PFrag = typename std::conditional<BF, bf16x8, float>::type;
+      PFrag pf[QB][BF ? 2 : 1];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (!((QM >> qb) & 1)) continue;
+        const float m_use = (m_run[qb] == RA_NEG_INF) ? 0.f : m_run[qb];
+        const float off = (b_raw[qb] - m_use) * c;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[qb][i] = fast_exp2(fmaf(s[qb][i], c, off));
+        float lsum = 0.f;
+        if constexpr (BF) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            pf[qb][h2] = pack_bf16x8(s[qb], 8 * h2);
+            lsum = sum_bf16x8(pf[qb][h2], lsum);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lsum += s[qb][i];
+        }
+        l_run[qb] += lsum;
+
+        // (5) Shaw: keys past the window go to bin 2k; keys inside it to
+        // their own bin: scattered into the wave's bin tile (one row per
+        // query), which is then multiplied by a_V with MFMA
+        if constexpr (KIND == 1) {
+          if (far_right[qb]) {
+            lr_run[qb] += lsum;
+          } else if (CLS == 2 && near[qb]) {
+            const int nbin = shaw_bin_slots(ck);
+            T* wrow = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes) + lq * nbin;
+            {
+              // this lane clears its half of the row: nbin/2 elements, 16-byte stores
+              constexpr int EPV = 16 / sizeof(T);
+              f32x4* zp = reinterpret_cast<f32x4*>(wrow + hh * (nbin / 2));
+              for (int x = 0; x < nbin / 2 / EPV; ++x) zp[x] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             wave_lds_fence();
-            const float* crow = cband + lq * kCbandStride + (pos[qb] - pq_min) + 31;
-            const float* prow = pband + lq * kPbandStride;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 pc = *reinterpret_cast<const f32x4*>(prow + 8 * g + 4 * hh);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) s[qb][kb][4 * g + e] = crow[-(8 * g + 4 * hh + e)] + pc[e];
-            }
-            wave_lds_fence();  // the next block overwrites both bands
-          }
-          s[qb][kb] = mma_frag<BF, D>(kf, qf[qb], s[qb][kb]);
-        }
-        // (3) masks: hidden keys become -inf (only on blocks that touch the
-        // causal diagonal or the end of the valid keys)
-        if ((a.causal && j0 + 31 > pq_min) || (j0 + 32 > kv_lim)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = j0 + acc_row(i, hh);
-            if (j >= kv_lim || (a.causal && j > pos[qb])) s[qb][kb][i] = RA_NEG_INF;
-          }
-        }
-      }
-    }
-
-    // (4) online softmax per query block, P to the PV operand layout
-    using PFrag = typename std::conditional<BF, bf16x8, float>::type;
-    PFrag pf[QB][BF ? kBK / 16 : 1];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = RA_NEG_INF;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-      mx = max_halves(mx);
-      const float cand = mx + b_raw[qb];
-      const bool need = cand > m_run[qb] + thr_raw;
-      if (__any(need)) {
-        const float m_new = need ? cand : m_run[qb];
-        const float alpha = fast_exp2((m_run[qb] - m_new) * c);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
-        l_run[qb] *= alpha;
-        lr_run[qb] *= alpha;
-        win_run[qb] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float m_use = (m_run[qb] == RA_NEG_INF) ? 0.f : m_run[qb];
-      const float off = (b_raw[qb] - m_use) * c;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[qb][kb][i] = fast_exp2(fmaf(s[qb][kb][i], c, off));
-      float lsum = 0.f;
-      if constexpr (BF) {
-#pragma unroll
-        for (int cc = 0; cc < kBK / 16; ++cc) {
-          pf[qb][cc] = pack_bf16x8(s[qb][cc >> 1], 8 * (cc & 1));
-          lsum = sum_bf16x8(pf[qb][cc], lsum);
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) lsum += s[qb][kb][i];
-      }
-      l_run[qb] += lsum;
-
-      // (5) Shaw: bins of this tile
-      if constexpr (KIND == 1) {
-        if (far_right[qb]) {
-          lr_run[qb] += lsum;
-        } else if (near[qb]) {
-          const int nbin = shaw_bin_slots(ck);
-          T* wsc = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes);
-          T* wrow = wsc + lq * nbin;
-          for (int x = hh * (nbin / 2); x < (hh + 1) * (nbin / 2); ++x) wrow[x] = (T)0.f;
-          wave_lds_fence();
-          float win = 0.f, lr = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+            float win = 0.f, lr = 0.f;
+            const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int offk = k0 + 32 * kb + acc_row(i, hh) - pos[qb];
+              const int offk = obase + acc_row(i, 0);
               float pv;
-              if constexpr (BF) pv = (float)pf[qb][2 * kb + (i >> 3)][i & 7];
-              else pv = s[qb][kb][i];
+              if constexpr (BF) pv = (float)pf[qb][i >> 3][i & 7];
+              else pv = s[qb][i];
               if (offk > -ck && offk < ck) {
                 wrow[offk + ck - 1] = (T)pv;
                 win += pv;
@@ -824,59 +969,91 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
                 lr += pv;
               }
             }
-          win_run[qb] += win;
-          lr_run[qb] += lr;
-          wave_lds_fence();
-          if constexpr (BF) {
-            const bf16* avt = reinterpret_cast<const bf16*>(smem + L.rel_off + L.avt_off);
-            for (int cb = 0; cb < nbin / 16; ++cb) {
-              const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 16 * cb + 8 * hh);
+            win_run[qb] += win;
+            lr_run[qb] += lr;
+            wave_lds_fence();
+            if constexpr (BF) {
+              const bf16* avt = reinterpret_cast<const bf16*>(smem + L.rel_off + L.avt_off);
+              for (int cb = 0; cb < nbin / 16; ++cb) {
+                const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 16 * cb + 8 * hh);
 #pragma unroll
-              for (int db = 0; db < NDB; ++db) {
-                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(avt + (32 * db + lq) * nbin + 16 * cb + 8 * hh);
-                o[qb][db] = mma_bf16(vf, wf, o[qb][db]);
+                for (int db = 0; db < NDB; ++db) {
+                  const bf16x8 vf = *reinterpret_cast<const bf16x8*>(avt + (32 * db + lq) * nbin + 16 * cb + 8 * hh);
+                  o[qb][db] = mma_bf16(vf, wf, o[qb][db]);
+                }
+              }
+            } else {
+              const float* av = reinterpret_cast<const float*>(a.table2);
+              for (int cb = 0; cb < nbin / 2; ++cb) {
+                const int rr = 2 * cb + hh;
+                const float wv = wrow[rr];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                  const float vv = rr < 2 * ck - 1 ? av[(size_t)(rr + 1) * D + 32 * db + lq] : 0.f;
+                  o[qb][db] = mma_f32(vv, wv, o[qb][db]);
+                }
               }
             }
-          } else {
-            const float* av = reinterpret_cast<const float*>(a.table2);
-            for (int cb = 0; cb < nbin / 2; ++cb) {
-              const int rr = 2 * cb + hh;
-              const float wv = wrow[rr];
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) {
-                const float vv = rr < 2 * ck - 1 ? av[(size_t)(rr + 1) * D + 32 * db + lq] : 0.f;
-                o[qb][db] = mma_f32(vv, wv, o[qb][db]);
-              }
-            }
+            wave_lds_fence();  // the next near block rewrites the bin tile
           }
-          wave_lds_fence();  // the next near tile rewrites the bin tile
         }
       }
-    }
 
-    // (6) O^T += V^T P^T; one V fragment feeds every query block
-    if constexpr (BF) {
+      // (6) O^T += V^T P^T over these 32 keys
+      if constexpr (BF) {
 #pragma unroll
-      for (int cc = 0; cc < kBK / 16; ++cc)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 vf = load_vt_frag<D>(vtile, cc, db, lane);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mma_bf16(vf, pf[qb][cc], o[qb][db]);
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
-          const int key = 32 * kb + acc_row(cc, hh);
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const float vv = load_v_f32<D>(vtile, key, 32 * db + lq);
+            const bf16x8 vf = load_vt_frag<D>(vtile, 2 * kb + h2, ko.v[db]);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mma_f32(vv, s[qb][kb][cc], o[qb][db]);
+            for (int qb = 0; qb < QB; ++qb)
+              if ((QM >> qb) & 1) o[qb][db] = mma_bf16(vf, pf[qb][h2], o[qb][db]);
           }
-        }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const float vv = load_v_f32<D>(vtile, kb, cc, db, ko.v[0]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              if ((QM >> qb) & 1) o[qb][db] = mma_f32(vv, s[qb][cc], o[qb][db]);
+          }
+      }
+    };
+
+    if constexpr (CLS != 2) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) step(std::integral_constant<int, (1 << QB) - 1>{}, kb);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) step(std::integral_constant<int, 1>{}, kb);
+      if constexpr (QB > 1) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) step(std::integral_constant<int, 2>{}, kb);
+      }
+    }
+  };
+
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  int r = 0;
+  while (r < n_my) {
+    const int cls = tile_class(r);
+    const int ln = opaque_lane();
+    if (cls == 0) {
+      do { run_tile(C0{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 0);
+    } else if (cls == 1) {
+      if constexpr (KIND == 0) {
+        do { run_tile(C1{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 1);
+      }
+    } else if (cls == 2) {
+      do { run_tile(C2{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 2);
+    } else {
+      do { run_tile(C3{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 3);
     }
   }
 
