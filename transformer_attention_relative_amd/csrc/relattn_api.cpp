@@ -295,7 +295,7 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
     a.t5_bidir = p->bidirectional ? 1 : 0; a.t5_nthr = P.t5.nthr;
     a.t5_lsat = P.t5.lsat; a.t5_rsat = P.t5.rsat;
     a.lut_lo = P.t5.lut_lo; a.lut_n = P.t5.lut_n;
-    for (int m = 0; m < P.t5.nthr; ++m) a.t5_thr[m] = P.t5.thr[m];
+    for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.t5.nthr ? P.t5.thr[m] : INT32_MAX;
   }
   hipError_t e = hipSuccess;
   if (p->kind == RELATTN_DEBERTA) {
@@ -330,7 +330,7 @@ relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, 
     if (s != RELATTN_OK) return s;
     a.t5_slots = P.slots; a.t5_exact = P.exact; a.t5_bidir = p->bidirectional ? 1 : 0;
     a.t5_nthr = P.nthr;
-    for (int m = 0; m < P.nthr; ++m) a.t5_thr[m] = P.thr[m];
+    for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.nthr ? P.thr[m] : INT32_MAX;
   } else {
     if (p->clip_k < 1) return fail(RELATTN_ERR_INVALID, "clip_k=%d must be >= 1", p->clip_k);
   }

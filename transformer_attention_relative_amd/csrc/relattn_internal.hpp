@@ -45,7 +45,7 @@ struct FwdArgs {
   int32_t t5_slots, t5_exact, t5_bidir, t5_nthr;
   int32_t t5_lsat, t5_rsat;  // offsets <= -lsat / >= rsat share one bucket
   int32_t lut_lo, lut_n;     // table covers offsets lut_lo .. lut_lo+lut_n-1
-  int32_t t5_thr[kT5MaxThr];
+  int32_t t5_thr[kT5MaxThr];  // entries from t5_nthr on hold INT32_MAX
 };
 
 struct IndexArgs {
@@ -54,7 +54,7 @@ struct IndexArgs {
   int64_t n;
   int32_t kind, which, clip_k;
   int32_t t5_slots, t5_exact, t5_bidir, t5_nthr;
-  int32_t t5_thr[kT5MaxThr];
+  int32_t t5_thr[kT5MaxThr];  // entries from t5_nthr on hold INT32_MAX
 };
 
 struct CombineArgs {

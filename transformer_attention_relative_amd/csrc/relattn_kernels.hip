@@ -83,6 +83,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // T5 bucket of offset = key - query ([RPE] T5 section; [T5B]).  thr[m] is the
 // smallest distance whose within-direction slot is >= exact + m (thr[0] ==
 // exact); the thresholds come from the host, so no logarithm runs here.
+// Entries from nthr on hold INT32_MAX, so with at most 16 thresholds the
+// count is a fixed run of compares against uniform (scalar) values.
 __device__ __forceinline__ int t5_bucket_dev(int offset, int slots, int exact, int bidir,
                                              int nthr, const int32_t* thr) {
   int base = 0, dist;
@@ -92,10 +94,14 @@ __device__ __forceinline__ int t5_bucket_dev(int offset, int slots, int exact, i
   } else {
     dist = offset < 0 ? -offset : 0;
   }
-  if (dist < exact) return base + dist;
   int m = 0;
-  for (int t = 1; t < nthr; ++t) m += dist >= thr[t] ? 1 : 0;
-  return base + exact + m;
+  if (nthr <= 16) {
+#pragma unroll
+    for (int t = 1; t < 16; ++t) m += dist >= thr[t] ? 1 : 0;
+  } else {
+    for (int t = 1; t < nthr; ++t) m += dist >= thr[t] ? 1 : 0;
+  }
+  return dist < exact ? base + dist : base + exact + m;
 }
 
 // Shaw row: clip(key - query, -k, k) + k ([RPE] Shaw section).
@@ -483,9 +489,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   const int wg_pos_max = a.q_pos_offset + min(q0 + BQ, a.Lq) - 1;
   const int ck = a.clip_k;
 
-  // ---- register loads first (Q fragments, the kind's small tables): the
-  // key/value stream is issued after them, so waiting for these values never
-  // waits for the stream (vector-memory counters retire in order) ----------
+  // ---- register loads first (valid length, Q fragments, the kind's small
+  // tables), all consumed by the prologue before the first key/value tile
+  // copy is issued: a wait for any of them then never waits for a tile ------
+  const int kv_valid = a.kv_valid_len ? __builtin_amdgcn_readfirstlane(a.kv_valid_len[b]) : a.Lk;
   TableFrag<BF, D> qf[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -543,32 +550,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     krow[0].load(kr + ((size_t)u * a.H + h) * D, hh);
   }
 
-  // ---- start streaming the first key tiles --------------------------------
-  Dma dma;
-  dma.init(wave, lane);
-  // Without a key split the first tiles are known before the valid length is
-  // read (tiles past it are loaded in bounds and never used).
-  const int reach0 = a.causal ? min(a.Lk, wg_pos_max + 1) : a.Lk;
-  const int n_pre0 = a.n_splits == 1 ? (reach0 + kBK - 1) / kBK : 0;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < n_pre0)
-      dma.issue(Kg, Vg, a.Lk, s * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
-
-  int kv_lim = a.Lk;
-  if (a.kv_valid_len) kv_lim = max(0, min(kv_lim, a.kv_valid_len[b]));
+  const int kv_lim = max(0, min(a.Lk, kv_valid));
   const int kv_end = a.causal ? min(kv_lim, wg_pos_max + 1) : kv_lim;
   const int n_kt = kv_end > 0 ? (kv_end + kBK - 1) / kBK : 0;
   const int per_split = (n_kt + a.n_splits - 1) / a.n_splits;
   const int kt_begin = min(n_kt, split * per_split);
   const int kt_end = min(n_kt, kt_begin + per_split);
   const int n_my = kt_end - kt_begin;
-  if (a.n_splits > 1) {
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < n_my)
-        dma.issue(Kg, Vg, a.Lk, (kt_begin + s) * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
-  }
 
   // ---- per-kind prologue (LDS tables) ---------------------------------------
   float shaw_right[QB];                              // Shaw: q.(a_K[2k] - a_K[0])
@@ -608,10 +596,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         if (rb * 32 >= nrow) break;
         const f32x16 acc = mma_frag0<BF, D>(krow[rb], qf[qb]);
         if (rb == 0) base0 = __shfl(acc[0], lq);  // row 0 sits in lane lq, register 0
+        // table rows past 2k land in the row's padding slot 2k+1
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = rb * 32 + acc_row(i, hh);
-          if (r < nrow) arel[(32 * qb + lq) * L.arel_stride + r] = acc[i] - base0;
+          const int r = min(rb * 32 + acc_row(i, hh), nrow);
+          arel[(32 * qb + lq) * L.arel_stride + r] = acc[i] - base0;
         }
       }
     }
@@ -640,6 +629,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       crow_lo[qb] = __shfl(acc[0], lq);
       crow_hi[qb] = __shfl(acc[1], lq);
     }
+  }
+
+  // ---- start streaming the first key tiles --------------------------------
+  {
+    Dma dma;
+    dma.init(wave, lane);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < n_my)
+        dma.issue(Kg, Vg, a.Lk, (kt_begin + s) * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
   }
 
   // ---- running state ------------------------------------------------------
