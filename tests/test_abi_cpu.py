@@ -118,7 +118,12 @@ def test_workspace_sizes():
     assert ra.relattn_workspace_bytes(p) == 0          # enough workgroups, no split
     p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=512, B=8, H=12,
                 Lq=2048, Lk=2048)
-    assert ra.relattn_workspace_bytes(p) >= 2 * 96 * 2048 * 4   # per-key constants
+    assert ra.relattn_workspace_bytes(p) == 0          # clipped blocks need no side buffer
+    # decode-like shape: few query tiles over a long key range -> split-KV partials
+    p = _params(kind="t5", table=FAKE, B=4, H=16, Lq=128, Lk=4096, q_pos_offset=3968,
+                causal=1, bidirectional=0)
+    n = ra.relattn_workspace_bytes(p)
+    assert n >= 2 * 64 * 128 * (64 + 2) * 4 and n % 256 == 0
 
 
 def test_rel_index_validation(lib):

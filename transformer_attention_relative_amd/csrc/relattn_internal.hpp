@@ -33,9 +33,8 @@ struct FwdArgs {
   const void *table, *table2;
   const int32_t *kv_valid_len;
   float *part_o;   // split-KV partial outputs  [n_splits][B*H][Lq][d]
-  float *part_ml;  // split-KV row stats        [n_splits][B*H][Lq][2] (m*c, l)
-  float *colc;     // DeBERTa per-key constants [2][B*H][Lk_pad]
-  int32_t B, H, Lq, Lk, Lk_pad;
+  float *part_ml;  // split-KV row stats        [n_splits][B*H][Lq][2] (log2 max, sum)
+  int32_t B, H, Lq, Lk;
   int32_t q_pos_offset, causal;
   int32_t clip_k;
   float scale;      // multiplies the raw score
@@ -63,12 +62,6 @@ struct CombineArgs {
   int32_t BH, Lq, n_splits;
 };
 
-struct ColcArgs {
-  const void *k, *qr;
-  float *colc;
-  int32_t BH, H, Lk, Lk_pad, clip_k;
-};
-
 // Kernel variant: waves per workgroup and 32-row query blocks per wave.
 struct Variant {
   int nw, qb;
@@ -86,7 +79,7 @@ RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k - 1) +
 // d elements, row-major; 16-byte chunks are XOR-swizzled within a row
 // (chunk c of row r sits in slot c ^ (r & 7)) so that column reads of
 // consecutive rows hit different banks.  After the stages, per kind:
-//   T5      float lut4[4][lut_stride]: four copies of bias[offset]/scale,
+//   T5      float lut4[4][lut_stride]: four copies of bias[offset]*log2(e),
 //           copy c shifted by c entries, so any 4 consecutive offsets are one
 //           aligned 16-byte read
 //   SHAW    per wave: float arel[rows][2k+1]; per wave: bin scratch

@@ -243,6 +243,17 @@ struct TableFrag<true, D> {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) v[t] = {};
   }
+  // x + y, rounded once to bfloat16 (nearest even)
+  __device__ __forceinline__ void sum_of(const TableFrag& x, const TableFrag& y) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 z = cvt2((float)x.v[t][e] + (float)y.v[t][e], (float)x.v[t][e + 1] + (float)y.v[t][e + 1]);
+        v[t][e] = z[0];
+        v[t][e + 1] = z[1];
+      }
+  }
 };
 template <int D>
 struct TableFrag<false, D> {
@@ -264,6 +275,10 @@ struct TableFrag<false, D> {
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int t = 0; t < D / 2; ++t) v[t] = 0.f;
+  }
+  __device__ __forceinline__ void sum_of(const TableFrag& x, const TableFrag& y) {
+#pragma unroll
+    for (int t = 0; t < D / 2; ++t) v[t] = x.v[t] + y.v[t];
   }
 };
 
@@ -431,10 +446,25 @@ struct TileDma {
 // The fused forward kernel
 // ----------------------------------------------------------------------------
 
+// A block whose lane partial row sum of P exceeds this (or is infinite)
+// goes through the exact path: its raw scores are recomputed, the reference
+// max moves to the block's max and the running state is rescaled.
+constexpr float kSumLimit = 0x1p20f;
+
+// Exponent offset c*b - m_ref of a row; a row with no reference yet (no
+// visible key so far) gets a huge finite offset, so every visible score of
+// its first block overflows to +inf (and takes the exact path) while hidden
+// scores stay -inf (p = 0).  Finite on purpose: -inf + inf would be NaN,
+// which the library's no-NaN arithmetic does not look for.
+__device__ __forceinline__ float ref_offset(float cb, float m_ref) {
+  return m_ref == RA_NEG_INF ? 0x1p100f : cb - m_ref;
+}
+
 template <int KIND, bool BF, int D, int QB, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a) {
   static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
   using T = typename std::conditional<BF, bf16, float>::type;
+  using QFrag = TableFrag<BF, D>;
   constexpr int NKB = kBK / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
   constexpr int RW = 32 * QB;         // query rows per wave
@@ -444,6 +474,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   constexpr int ROWB = Dma::ROWB;     // bytes per K / V row
   constexpr int LPW = Dma::LPW;       // load instructions per wave per tile
   constexpr bool EVEN_LOADS = (Dma::IPT % NW) == 0;
+  constexpr float NEG_INF = RA_NEG_INF;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const LdsLayout L = lds_layout(KIND, BF, D, QB, NW, a.clip_k, a.lut_n);
@@ -474,15 +505,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   const int pw_min = a.q_pos_offset + wrow0;
   const bool wave_active = wrow0 < a.Lq;
   const int pw_max_real = a.q_pos_offset + min(wrow0 + RW, a.Lq) - 1;
-  int qrow[QB], pos[QB];
+  int qrow[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = wrow0 + 32 * qb + lq;
-    pos[qb] = a.q_pos_offset + qrow[qb];
-  }
+  for (int qb = 0; qb < QB; ++qb) qrow[qb] = wrow0 + 32 * qb + lq;
 
+  // p = exp2(c * s + (c * b - m_ref)): one FMA per score, c = scale*log2(e),
+  // b the block's per-row constant, m_ref the row's reference (log2 units)
   const float c = a.scale_log2;
-  const float thr_raw = 8.0f / c;  // lazy rescale threshold in raw score units
   const T* Qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * a.Lq * D;
   const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + (size_t)bh * a.Lk * D);
   const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + (size_t)bh * a.Lk * D);
@@ -493,20 +522,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   // tables), all consumed by the prologue before the first key/value tile
   // copy is issued: a wait for any of them then never waits for a tile ------
   const int kv_valid = a.kv_valid_len ? __builtin_amdgcn_readfirstlane(a.kv_valid_len[b]) : a.Lk;
-  TableFrag<BF, D> qf[QB];
+  QFrag qf[QB];
+  // DeBERTa: q + Qr[0] and q + Qr[2k-1] (rounded once to the input type).
+  // Where every offset of a block is clipped, q.k + k.Qr[d(j,i)] equals
+  // (q + Qr[d]).k with a single Qr row, so the position-to-content term of
+  // such blocks rides on the content MFMA.
+  QFrag qside[KIND == 2 ? QB : 1][KIND == 2 ? 2 : 1];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (qrow[qb] < a.Lq) qf[qb].load(Qg + (size_t)qrow[qb] * D, hh);
     else qf[qb].zero();
   }
+  if constexpr (KIND == 2) {
+    const T* qr = reinterpret_cast<const T*>(a.table2);
+    QFrag r0, r1;
+    r0.load(qr + (size_t)h * D, hh);
+    r1.load(qr + ((size_t)(2 * ck - 1) * a.H + h) * D, hh);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      qside[qb][0].sum_of(qf[qb], r0);
+      qside[qb][1].sum_of(qf[qb], r1);
+    }
+  }
   constexpr int LUT_EARLY = 8;  // offset-table entries per thread fetched early
   float lut_early[LUT_EARLY];
-  float bias_left_raw = 0.f, bias_right_raw = 0.f;  // T5 saturated buckets / scale
+  float bias_left = 0.f, bias_right = 0.f;          // T5 saturated buckets / scale
   constexpr int SHAW_RB = 3;                          // blocks of 32 a_K rows (k <= 32)
   TableFrag<BF, D> krow[KIND == 1 ? SHAW_RB : 1];     // Shaw a_K rows / DeBERTa Kr rows
   constexpr int AVT_EARLY = 8;
   T avt_early[AVT_EARLY];
-  const float inv_scale = 1.f / a.scale;
   if constexpr (KIND == 0) {
     const float* tab = reinterpret_cast<const float*>(a.table);
 #pragma unroll
@@ -523,8 +567,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     }
     const int bl = t5_bucket_dev(-(1 << 30), a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
     const int br = t5_bucket_dev(1 << 30, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
-    bias_left_raw = tab[bl * a.H + h] * inv_scale;
-    bias_right_raw = tab[br * a.H + h] * inv_scale;
+    const float inv_scale = 1.f / a.scale;
+    bias_left = tab[bl * a.H + h] * inv_scale;
+    bias_right = tab[br * a.H + h] * inv_scale;
   } else if constexpr (KIND == 1) {
     const T* ak = reinterpret_cast<const T*>(a.table);
     const int nrow = 2 * ck + 1;
@@ -567,6 +612,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 
   if constexpr (KIND == 0) {
     // four copies of bias[offset]/scale, copy c shifted by c entries
+    const float inv_scale = 1.f / a.scale;
 #pragma unroll
     for (int i = 0; i < LUT_EARLY; ++i) {
       const int e = tid + i * 64 * NW;
@@ -583,9 +629,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       relf[e] = val;
     }
   } else if constexpr (KIND == 1) {
-    // arel[row][r] = q.a_K[r] - q.a_K[0], r = 0..2k, by MFMA over blocks of 32
-    // table rows; subtracting the r = 0 value is softmax-neutral and makes
-    // every key beyond -k contribute exactly zero.
+    // arel[row][r] = q.a_K[r] - q.a_K[0], r = 0..2k, by MFMA over blocks of
+    // 32 table rows; subtracting the r = 0 value is softmax-neutral and
+    // makes every key beyond -k contribute exactly zero.
     arel = relf + wave * L.arel_wave_floats;
     const int nrow = 2 * ck + 1;
 #pragma unroll
@@ -642,13 +688,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   }
 
   // ---- running state ------------------------------------------------------
+  // m_ref: the row's reference max in log2 units (both lane halves agree);
+  // -inf until the row has seen a visible key.  p = exp2(s - m_ref) is used
+  // as is while every block keeps its lane sums below kSumLimit.
   f32x16 o[QB][NDB];
-  float m_run[QB], l_run[QB], lr_run[QB], win_run[QB];
+  float m_ref[QB], l_run[QB], lr_run[QB], win_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[qb][db] = {};
-    m_run[qb] = RA_NEG_INF;  // raw-score reference max (both halves agree)
+    m_ref[qb] = NEG_INF;
     l_run[qb] = 0.f;         // this lane's partial row sum
     lr_run[qb] = 0.f;        // Shaw: partial mass of keys at offset >= k
     win_run[qb] = 0.f;       // Shaw: partial mass of keys inside the clip window
@@ -656,7 +705,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 
   // Tile classes (wave-uniform):
   //   0: every block far from the diagonal band (the relative term is a
-  //      per-row constant, or a per-key constant for DeBERTa), no mask;
+  //      per-row constant, plus a Qr row folded into the query for DeBERTa),
+  //      no mask;
   //   1: T5, every block inside the bucket table's range, no mask;
   //   2: anything else (band terms, masks, Shaw bins);
   //   3: nothing to do for this wave (past its causal reach).
@@ -693,8 +743,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     for (int qb = 0; qb < QB; ++qb) pos[qb] = pw_min + 32 * qb + lq;
     KOffsets<BF, D> ko;
     ko.init(lane);
-    Dma dma;
-    dma.init(wave, lane);
     const int kt = kt_begin + r;
     if constexpr (NS >= 3 && EVEN_LOADS) {
       // tiles newer than r that may still be in flight: min(NS - 2, n_my - 1 - r)
@@ -707,49 +755,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     }
     __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     const int k0 = kt * kBK;
-    // DeBERTa per-key constants of clipped blocks are requested before the
-    // next tiles, so waiting for them never waits for the prefetch
-    f32x4 colv[QB][NKB][4];
-    if constexpr (KIND == 2) {
-      if (CLS != 3) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const int pq_min = pw_min + 32 * qb, j0 = k0 + 32 * kb;
-            const int tmin = pq_min - (j0 + 31), tmax = pq_min + 31 - j0;
-            const int side = tmin >= ck ? 0 : (tmax <= -ck ? 1 : -1);
-            if (side >= 0) {
-              const float* cc = a.colc + ((size_t)side * a.B * a.H + bh) * a.Lk_pad + j0;
-#pragma unroll
-              for (int g = 0; g < 4; ++g) colv[qb][kb][g] = *reinterpret_cast<const f32x4*>(cc + 8 * g + 4 * hh);
-            }
-          }
-      }
-    }
-    if (r + NS - 1 < n_my)
+    if (r + NS - 1 < n_my) {
+      // copy offsets from a fresh lane id: kept out of registers between tiles
+      Dma dma;
+      dma.init(wave, opaque_lane());
       dma.issue(Kg, Vg, a.Lk, (kt + NS - 1) * kBK, smem + ((r + NS - 1) % NS) * L.stage_bytes,
                 L.tile_bytes, wave, lane);
+    }
     if constexpr (CLS == 3) return;
     const char* ktile = smem + (r % NS) * L.stage_bytes;
     const char* vtile = ktile + L.tile_bytes;
 
     // ---- the tile's query blocks (wave-uniform) ----
-    float b_raw[QB];
+    float b_tile[QB];  // per-row constant of the tile's far blocks (raw score units)
     bool near[QB], far_right[QB];
     int deb_side[QB];  // DeBERTa: 0 far-left tile, 1 far-right tile, -1 mixed
     const float* lutp[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      b_raw[qb] = 0.f;
+      b_tile[qb] = 0.f;
       near[qb] = far_right[qb] = false;
       deb_side[qb] = -1;
       lutp[qb] = nullptr;
       const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
       const int omin = k0 - pq_max, omax = k0 + kBK - 1 - pq_min;  // key - query
       if constexpr (KIND == 0) {
-        if (omax <= -a.t5_lsat) b_raw[qb] = bias_left_raw;
-        else if (omin >= a.t5_rsat) b_raw[qb] = bias_right_raw;
+        if (omax <= -a.t5_lsat) b_tile[qb] = bias_left;
+        else if (omin >= a.t5_rsat) b_tile[qb] = bias_right;
         else {
           near[qb] = true;
           const int x0 = k0 - pos[qb] - a.lut_lo;  // table index of this lane's first key
@@ -758,191 +790,224 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         }
       } else if constexpr (KIND == 1) {
         if (omin >= ck) {
-          b_raw[qb] = shaw_right[qb];
+          b_tile[qb] = shaw_right[qb];
           far_right[qb] = true;
         } else if (omax > -ck) {
           near[qb] = true;
         }
       } else {
-        if (-omax >= ck) { deb_side[qb] = 0; b_raw[qb] = crow_hi[qb]; }       // every query - key >= k
-        else if (-omin <= -ck) { deb_side[qb] = 1; b_raw[qb] = crow_lo[qb]; } // every query - key <= -k
+        if (-omax >= ck) { deb_side[qb] = 0; b_tile[qb] = crow_hi[qb]; }       // every query - key >= k
+        else if (-omin <= -ck) { deb_side[qb] = 1; b_tile[qb] = crow_lo[qb]; } // every query - key <= -k
       }
     }
+    // exponent offsets c*b - m_ref of the tile's blocks
+    float off[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) off[qb] = ref_offset(c * b_tile[qb], m_ref[qb]);
 
     // One step of 32 keys (block kb of the tile) for the query blocks in the
-    // bit mask QM: scores, online softmax, P V.  A K fragment and a V fragment
-    // read from LDS feed every query block of the step.  Class 2 runs one
-    // query block per step so that fewer values are live.
+    // bit mask QM: scores, softmax, P V.  A K fragment and a V fragment read
+    // from LDS feed every query block of the step.  Class 2 runs one query
+    // block per step so that fewer values are live.
     auto step = [&](auto qm_tag, const int kb) {
       constexpr int QM = decltype(qm_tag)::value;
       const int j0 = k0 + 32 * kb;
+
+      // DeBERTa, per block: 0 / 1 every offset clipped on one side, -1 band
+      auto deb_block_side = [&](const int qb) -> int {
+        const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
+        const int tmin = pq_min - (j0 + 31), tmax = pq_max - j0;  // query - key over the block
+        return tmin >= ck ? 0 : (tmax <= -ck ? 1 : -1);
+      };
+      // per-row constant of this block (raw score units)
+      auto b_block = [&](const int qb) -> float {
+        if constexpr (KIND == 2) {
+          if (CLS == 2) {
+            const int side = deb_block_side(qb);
+            return side == 0 ? crow_hi[qb] : (side == 1 ? crow_lo[qb] : 0.f);
+          }
+        }
+        return b_tile[qb];
+      };
+
+      // raw scores of query block qb: relative term (except a per-row
+      // constant) + q.k; hidden keys -inf
+      auto scores = [&](const int qb, const TableFrag<BF, D>& kf) -> f32x16 {
+        const int pq_min = pw_min + 32 * qb;
+        f32x16 s;
+        if constexpr (KIND == 0) {
+          if (CLS == 1 || (CLS == 2 && near[qb])) {
+            f32x16 init;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(lutp[qb] + 32 * kb + 8 * g + 4 * hh);
+              init[4 * g + 0] = x[0]; init[4 * g + 1] = x[1];
+              init[4 * g + 2] = x[2]; init[4 * g + 3] = x[3];
+            }
+            s = mma_frag<BF, D>(kf, qf[qb], init);
+          } else {
+            s = mma_frag0<BF, D>(kf, qf[qb]);
+          }
+        } else if constexpr (KIND == 1) {
+          if (CLS == 2 && near[qb]) {
+            const float* ar = arel + (32 * qb + lq) * L.arel_stride;
+            const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
+            f32x16 init;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) init[i] = ar[shaw_row_dev(obase + acc_row(i, 0), ck)];
+            s = mma_frag<BF, D>(kf, qf[qb], init);
+          } else {
+            s = mma_frag0<BF, D>(kf, qf[qb]);
+          }
+        } else {
+          const int side = CLS == 0 ? deb_side[qb] : deb_block_side(qb);
+          if (side >= 0) {
+            s = mma_frag0<BF, D>(kf, side == 0 ? qside[qb][0] : qside[qb][1]);
+          } else {
+            float* cband = relf + wave * L.deb_wave_floats;
+            float* pband = cband + kBlockRows * kCbandStride;
+            const T* kr = reinterpret_cast<const T*>(a.table);
+            const T* qr = reinterpret_cast<const T*>(a.table2);
+            const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
+            // content-to-position: rows Kr[delta(T0 + m)], columns = queries
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+              TableFrag<BF, D> af;
+              af.load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
+              const f32x16 acc = mma_frag0<BF, D>(af, qf[qb]);
+              float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+                *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
+              }
+            }
+            // position-to-content: rows = keys, columns n <-> query - key =
+            // T0 + n, Qr row delta(key - query); scattered to [query][key]
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const int n = 32 * nb + lq;
+              TableFrag<BF, D> bfr;
+              bfr.load(qr + ((size_t)deberta_delta_dev(-(T0 + n), ck) * a.H + h) * D, hh);
+              const f32x16 acc = mma_frag0<BF, D>(kf, bfr);
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int jl = acc_row(i, hh);
+                const int sq = n + jl - 31;
+                if (sq >= 0 && sq < 32) pband[sq * kPbandStride + jl] = acc[i];
+              }
+            }
+            wave_lds_fence();
+            const float* crow = cband + lq * kCbandStride + (pos[qb] - pq_min) + 31;
+            const float* prow = pband + lq * kPbandStride;
+            f32x16 init;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 pc = *reinterpret_cast<const f32x4*>(prow + 8 * g + 4 * hh);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) init[4 * g + e] = crow[-(8 * g + 4 * hh + e)] + pc[e];
+            }
+            wave_lds_fence();  // the next block overwrites both bands
+            s = mma_frag<BF, D>(kf, qf[qb], init);
+          }
+        }
+        // masks: hidden keys become -inf (only on blocks that touch the
+        // causal diagonal or the end of the valid keys)
+        if constexpr (CLS == 2) {
+          if ((a.causal && j0 + 31 > pq_min) || (j0 + 32 > kv_lim)) {
+            // register i holds key j0 + acc_row(i, hh) = j0 + 4hh + acc_row(i, 0);
+            // it is visible iff acc_row(i, 0) <= last - j0 - 4hh
+            const int last = a.causal ? min(kv_lim - 1, pos[qb]) : kv_lim - 1;
+            const int lim = last - j0 - 4 * hh;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (acc_row(i, 0) > lim) s[i] = NEG_INF;
+          }
+        }
+        return s;
+      };
+
+      using PFrag = typename std::conditional<BF, bf16x8, float>::type;
+      PFrag pf[QB][BF ? 2 : 1];
       f32x16 s[QB];
+      float lsum[QB];
+      // p = exp2(mul * s + add) in place of s, its bfloat16 copy for the P V
+      // product, the lane sum
+      auto softmax = [&](const int qb, const float mul, const float add) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[qb][i] = fast_exp2(fmaf(s[qb][i], mul, add));
+        float ls = 0.f;
+        if constexpr (BF) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            pf[qb][h2] = pack_bf16x8(s[qb], 8 * h2);
+            ls = sum_bf16x8(pf[qb][h2], ls);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ls += s[qb][i];
+        }
+        lsum[qb] = ls;
+      };
+
+      // Scores of every query block of the step, their softmax, then one
+      // wave-wide check: the whole step stays one scheduling region, so the
+      // MFMAs of one query block overlap the exponentials of the other.  One
+      // K fragment read from LDS feeds the query blocks; the exact path reads
+      // its own copy, so nothing of the fast path stays live for it.
       {
         TableFrag<BF, D> kf;
         kf.load_lds(ktile + 32 * kb * ROWB, ko.k);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           if (!((QM >> qb) & 1)) continue;
-          const int pq_min = pw_min + 32 * qb, pq_max = pq_min + 31;
-          // (1)+(2) relative term into the accumulator, then S^T += K Q^T on top
-          // (far blocks start from the MFMA's zero accumulator input)
-          if constexpr (KIND == 0) {
-            if (CLS == 1 || (CLS == 2 && near[qb])) {
-              f32x16 init;
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(lutp[qb] + 32 * kb + 8 * g + 4 * hh);
-                init[4 * g + 0] = x[0]; init[4 * g + 1] = x[1];
-                init[4 * g + 2] = x[2]; init[4 * g + 3] = x[3];
-              }
-              s[qb] = mma_frag<BF, D>(kf, qf[qb], init);
-            } else {
-              s[qb] = mma_frag0<BF, D>(kf, qf[qb]);
-            }
-          } else if constexpr (KIND == 1) {
-            if (CLS == 2 && near[qb]) {
-              const float* ar = arel + (32 * qb + lq) * L.arel_stride;
-              const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
-              f32x16 init;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) init[i] = ar[shaw_row_dev(obase + acc_row(i, 0), ck)];
-              s[qb] = mma_frag<BF, D>(kf, qf[qb], init);
-            } else {
-              s[qb] = mma_frag0<BF, D>(kf, qf[qb]);
-            }
-          } else {
-            const int tmin = pq_min - (j0 + 31), tmax = pq_max - j0;  // query - key over the block
-            int side = -1;
-            if (tmin >= ck) side = 0;
-            else if (tmax <= -ck) side = 1;
-            if (CLS == 0 || side >= 0) {
-              // per-key constant k_j.Qr[0] (side 0) or k_j.Qr[2k-1] (side 1); the
-              // per-row constant is folded into the exponent for whole-tile
-              // sides, else added here
-              const float add = (CLS == 0 || deb_side[qb] >= 0) ? 0.f : (side == 0 ? crow_hi[qb] : crow_lo[qb]);
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const f32x4 x = colv[qb][kb][g];
-                s[qb][4 * g + 0] = x[0] + add; s[qb][4 * g + 1] = x[1] + add;
-                s[qb][4 * g + 2] = x[2] + add; s[qb][4 * g + 3] = x[3] + add;
-              }
-            } else {
-              float* cband = relf + wave * L.deb_wave_floats;
-              float* pband = cband + kBlockRows * kCbandStride;
-              const T* kr = reinterpret_cast<const T*>(a.table);
-              const T* qr = reinterpret_cast<const T*>(a.table2);
-              const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
-              // content-to-position: rows Kr[delta(T0 + m)], columns = queries
-#pragma unroll
-              for (int tb = 0; tb < 2; ++tb) {
-                TableFrag<BF, D> af;
-                af.load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
-                const f32x16 acc = mma_frag0<BF, D>(af, qf[qb]);
-                float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-                  *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
-                }
-              }
-              // position-to-content: rows = keys, columns n <-> query - key =
-              // T0 + n, Qr row delta(key - query); scattered to [query][key]
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb) {
-                const int n = 32 * nb + lq;
-                TableFrag<BF, D> bfr;
-                bfr.load(qr + ((size_t)deberta_delta_dev(-(T0 + n), ck) * a.H + h) * D, hh);
-                const f32x16 acc = mma_frag0<BF, D>(kf, bfr);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                  const int jl = acc_row(i, hh);
-                  const int sq = n + jl - 31;
-                  if (sq >= 0 && sq < 32) pband[sq * kPbandStride + jl] = acc[i];
-                }
-              }
-              wave_lds_fence();
-              const float* crow = cband + lq * kCbandStride + (pos[qb] - pq_min) + 31;
-              const float* prow = pband + lq * kPbandStride;
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const f32x4 pc = *reinterpret_cast<const f32x4*>(prow + 8 * g + 4 * hh);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[qb][4 * g + e] = crow[-(8 * g + 4 * hh + e)] + pc[e];
-              }
-              wave_lds_fence();  // the next block overwrites both bands
-            }
-            s[qb] = mma_frag<BF, D>(kf, qf[qb], s[qb]);
-          }
-          // (3) masks: hidden keys become -inf (only on blocks that touch the
-          // causal diagonal or the end of the valid keys)
-          if constexpr (CLS == 2) {
-            if ((a.causal && j0 + 31 > pq_min) || (j0 + 32 > kv_lim)) {
-              // register i holds key j0 + acc_row(i, hh) = j0 + 4hh + acc_row(i, 0);
-              // it is visible iff acc_row(i, 0) <= last - j0 - 4hh
-              const int last = a.causal ? min(kv_lim - 1, pos[qb]) : kv_lim - 1;
-              const int lim = last - j0 - 4 * hh;
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                if (acc_row(i, 0) > lim) s[qb][i] = RA_NEG_INF;
-            }
-          }
+          s[qb] = scores(qb, kf);
         }
       }
-
-      // (4) online softmax: row max (v_max3 pairs, then across the two lane
-      // halves); the reference max moves only when a block's max exceeds it
-      // by more than 2^8, for all query blocks of the step under one branch
-      float cand[QB];
-      bool need_any = false;
+      bool bad = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (!((QM >> qb) & 1)) continue;
-        cand[qb] = max_halves(max16(s[qb])) + b_raw[qb];
-        need_any = need_any || (cand[qb] > m_run[qb] + thr_raw);
+        softmax(qb, c, (KIND == 2 && CLS == 2) ? ref_offset(c * b_block(qb), m_ref[qb]) : off[qb]);
+        bad = bad || lsum[qb] > kSumLimit;
       }
-      if (__any(need_any)) {
+      if (__builtin_expect(__any(bad), 0)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           if (!((QM >> qb) & 1)) continue;
-          const bool need = cand[qb] > m_run[qb] + thr_raw;
-          const float m_new = need ? cand[qb] : m_run[qb];
-          const float alpha = fast_exp2((m_run[qb] - m_new) * c);
+          if (!__any(lsum[qb] > kSumLimit)) continue;
+          // exact path: scores in log2 units, the row max, rescale of the
+          // running state
+          TableFrag<BF, D> kf2;
+          kf2.load_lds(ktile + 32 * kb * ROWB, ko.k);
+          s[qb] = scores(qb, kf2);
+          const float cb = c * b_block(qb);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[qb][i] = fmaf(s[qb][i], c, cb);
+          const float mn = fmaxf(m_ref[qb], max_halves(max16(s[qb])));
+          const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m_ref[qb] - mn);
 #pragma unroll
           for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
           l_run[qb] *= alpha;
           lr_run[qb] *= alpha;
           win_run[qb] *= alpha;
-          m_run[qb] = m_new;
+          m_ref[qb] = mn;
+          const float mu = mn == NEG_INF ? 0.f : mn;
+          softmax(qb, 1.f, -mu);
+          off[qb] = ref_offset(c * b_tile[qb], m_ref[qb]);
         }
       }
-      using PFrag = typename std::conditional<BF, bf16x8, float>::type;
-      PFrag pf[QB][BF ? 2 : 1];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (!((QM >> qb) & 1)) continue;
-        const float m_use = (m_run[qb] == RA_NEG_INF) ? 0.f : m_run[qb];
-        const float off = (b_raw[qb] - m_use) * c;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[qb][i] = fast_exp2(fmaf(s[qb][i], c, off));
-        float lsum = 0.f;
-        if constexpr (BF) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            pf[qb][h2] = pack_bf16x8(s[qb], 8 * h2);
-            lsum = sum_bf16x8(pf[qb][h2], lsum);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) lsum += s[qb][i];
-        }
-        l_run[qb] += lsum;
+        l_run[qb] += lsum[qb];
 
-        // (5) Shaw: keys past the window go to bin 2k; keys inside it to
-        // their own bin: scattered into the wave's bin tile (one row per
-        // query), which is then multiplied by a_V with MFMA
+        // Shaw: keys past the window go to bin 2k; keys inside it to their
+        // own bin: scattered into the wave's bin tile (one row per query),
+        // which is then multiplied by a_V with MFMA
         if constexpr (KIND == 1) {
           if (far_right[qb]) {
-            lr_run[qb] += lsum;
+            lr_run[qb] += lsum[qb];
           } else if (CLS == 2 && near[qb]) {
             const int nbin = shaw_bin_slots(ck);
             T* wrow = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes) + lq * nbin;
@@ -998,7 +1063,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         }
       }
 
-      // (6) O^T += V^T P^T over these 32 keys
+      // O^T += V^T P^T over these 32 keys
       if constexpr (BF) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -1062,7 +1127,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const float m_use = (m_run[qb] == RA_NEG_INF) ? 0.f : m_run[qb];
     if constexpr (KIND == 1) {
       // bins 0 and 2k take the row mass not held by the in-window bins
       const T* av = reinterpret_cast<const T*>(a.table2);
@@ -1109,7 +1173,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
           *reinterpret_cast<f32x4*>(po + dd) = y;
         }
       if (hh == 0) {
-        const f32x2 ml = {l_tot > 0.f ? m_use * c : RA_NEG_INF, l_tot};
+        const f32x2 ml = {l_tot > 0.f ? m_ref[qb] : NEG_INF, l_tot};
         *reinterpret_cast<f32x2*>(a.part_ml + row * 2) = ml;
       }
     }
@@ -1151,34 +1215,6 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
     const f32x4 y = acc * inv;
     *reinterpret_cast<f32x4*>(og) = y;
   }
-}
-
-// DeBERTa per-key constants for blocks whose offsets are all clipped:
-// colc[0][bh][j] = k_j . Qr[0][h] (key far before the query: d(j,i) = 0),
-// colc[1][bh][j] = k_j . Qr[2k-1][h] (key far after it).  Keys in the
-// padding up to Lk_pad get 0.
-template <bool BF, int D>
-__global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
-  using T = typename std::conditional<BF, bf16, float>::type;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.BH * a.Lk_pad;
-  if (idx >= total) return;
-  const int bh = (int)(idx / a.Lk_pad), j = (int)(idx % a.Lk_pad);
-  const int h = bh % a.H;
-  float s0 = 0.f, s1 = 0.f;
-  if (j < a.Lk) {
-    const T* kr = reinterpret_cast<const T*>(a.k) + ((size_t)bh * a.Lk + j) * D;
-    const T* q0 = reinterpret_cast<const T*>(a.qr) + (size_t)h * D;
-    const T* q1 = reinterpret_cast<const T*>(a.qr) + ((size_t)(2 * a.clip_k - 1) * a.H + h) * D;
-#pragma unroll 8
-    for (int e = 0; e < D; ++e) {
-      const float kv = (float)kr[e];
-      s0 = fmaf(kv, (float)q0[e], s0);
-      s1 = fmaf(kv, (float)q1[e], s1);
-    }
-  }
-  a.colc[(size_t)bh * a.Lk_pad + j] = s0;
-  a.colc[((size_t)a.BH + bh) * a.Lk_pad + j] = s1;
 }
 
 // ----------------------------------------------------------------------------
@@ -1225,16 +1261,6 @@ hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) 
   else if (bf && d == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
   else if (!bf && d == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st) {
-  const int64_t threads = (int64_t)a.BH * a.Lk_pad;
-  const int grid = (int)((threads + 255) / 256);
-  if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
-  else if (bf && d == 32) hipLaunchKernelGGL((relattn_colc_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
-  else if (!bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((relattn_colc_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
