@@ -123,8 +123,9 @@ relattn_status relattn_fwd(const relattn_params *p, const void *q, const void *k
                            const void *v, void *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace relattn_fwd needs for this problem (the split-KV
- * partial results of decode-like shapes; 0 when the key range is not split). */
+/* Bytes of device workspace relattn_fwd needs for this problem: the split-KV
+ * partial results of decode-like shapes, and for DEBERTA the per-key
+ * position-to-content constants of clipped blocks (8 bytes per key). */
 relattn_status relattn_workspace_bytes(const relattn_params *p, size_t *bytes);
 
 /*

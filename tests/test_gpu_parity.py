@@ -294,3 +294,62 @@ def test_shaw_bins_readout_through_fused_kernel():
             if vis.sum():
                 want[i] = np.bincount(idx[i][vis], minlength=2 * kc + 1) / vis.sum()
         np.testing.assert_allclose(got, want, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# 5. the online softmax's reference max: scores that grow along the keys make
+#    it move many times; a late jump far above every earlier score overflows
+#    the running reference and must be caught before it reaches the output
+# ----------------------------------------------------------------------------
+
+def _ramped(wl, inp, lo, hi, q_mul):
+    """K rows scaled by a ramp from lo to hi along the key axis, Q by q_mul,
+    rounded back to the workload dtype (the oracle sees the same values)."""
+    ramp = torch.linspace(lo, hi, wl.Lk).reshape(1, 1, wl.Lk, 1)
+    k = (inp["k"].float() * ramp).to(wl.torch_dtype)
+    q = (inp["q"].float() * q_mul).to(wl.torch_dtype)
+    return dict(inp, k=k, q=q)
+
+
+RAMP_CASES = [
+    _small("t5", "fp32", 64, Lq=200, Lk=700),
+    _small("t5", "bf16", 64, Lq=260, Lk=700, valid_len_range=(300, 700)),
+    _small("shaw", "fp32", 64, clip_k=16, causal=True, Lq=700, Lk=700),
+    _small("shaw", "bf16", 64, clip_k=8, Lq=260, Lk=700),
+    _small("deberta", "fp32", 64, clip_k=64, Lq=200, Lk=700),
+    _small("deberta", "bf16", 64, clip_k=100, causal=True, Lq=700, Lk=700),
+]
+
+
+# Logits here reach ~45 log2 units, where float32 itself carries ~|s| 2^-24
+# sqrt(d) ~ 2e-5 of relative error into p: the float32 bar for these stress
+# inputs is 2e-4 max-abs / 2e-5 mean-abs (the 1e-5 bar is for the workloads'
+# N(0, 1) inputs); bfloat16 keeps its bar.
+STRESS_TOL = {"fp32": (2e-4, 2e-5), "bf16": TOL["bf16"]}
+
+
+@pytest.mark.parametrize("wl", RAMP_CASES, ids=_case_id)
+def test_reference_moves_with_growing_scores(wl):
+    # logits grow from ~0 to ~+-45 log2 units along the keys
+    inp = _ramped(wl, make_inputs(wl, seed=21), 0.05, 6.0, 1.5)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    err = np.abs(got - want)
+    assert np.isfinite(got).all()
+    assert err.max() <= STRESS_TOL[wl.dtype][0], err.max()
+    assert err.mean() <= STRESS_TOL[wl.dtype][1], err.mean()
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+def test_late_score_jump_is_exact(kind):
+    # the last 40 keys score ~10x higher than the rest: their exponentials
+    # overflow the running reference (exp2 of hundreds), which the kernel must
+    # detect and redo exactly
+    wl = _small(kind, "bf16", 64, Lq=130, Lk=600, clip_k=16 if kind != "t5" else 0)
+    inp = make_inputs(wl, seed=22)
+    k = inp["k"].float()
+    k[:, :, -40:] *= 12.0
+    inp = dict(inp, k=k.to(wl.torch_dtype), q=(inp["q"].float() * 2.0).to(wl.torch_dtype))
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    check_close(got, want, wl.dtype, f"{kind} jump")

@@ -17,6 +17,7 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
                       hipStream_t st);
 bool fwd_variant_built(int kind, bool bf, Variant v);
 hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st);
+hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st);
 hipError_t launch_index(const IndexArgs& a, hipStream_t st);
 }  // namespace relattn
 
@@ -102,7 +103,7 @@ struct Plan {
   float scale;
   Variant var;
   int n_qtiles, n_splits, grid, lds;
-  size_t off_part_o, off_part_ml, ws_bytes;
+  size_t off_part_o, off_part_ml, off_colc, ws_bytes;
   T5Plan t5;
 };
 
@@ -202,12 +203,16 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   P->lds = lds_total;
 
   size_t off = 0;
-  P->off_part_o = P->off_part_ml = 0;
+  P->off_part_o = P->off_part_ml = P->off_colc = 0;
   if (splits > 1) {
     P->off_part_o = off;
     off = align256(off + (size_t)splits * BH * p->Lq * p->d * sizeof(float));
     P->off_part_ml = off;
     off = align256(off + (size_t)splits * BH * p->Lq * 2 * sizeof(float));
+  }
+  if (p->kind == RELATTN_DEBERTA) {
+    P->off_colc = off;
+    off = align256(off + (size_t)BH * p->Lk * 8);
   }
   P->ws_bytes = off;
   return RELATTN_OK;
@@ -292,6 +297,12 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
     for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.t5.nthr ? P.t5.thr[m] : INT32_MAX;
   }
   hipError_t e = hipSuccess;
+  if (p->kind == RELATTN_DEBERTA) {
+    a.colc = ws + P.off_colc;
+    ColcArgs ca{k, p->table2, ws + P.off_colc, p->B * p->H, p->H, p->Lk, p->clip_k};
+    e = launch_colc(P.bf, p->d, ca, st);
+    if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "colc launch: %s", hipGetErrorString(e));
+  }
   e = launch_fwd(p->kind, P.bf, p->d, P.var, a, P.grid, P.lds, st);
   if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   if (P.n_splits > 1) {

@@ -34,6 +34,7 @@ struct FwdArgs {
   const int32_t *kv_valid_len;
   float *part_o;   // split-KV partial outputs  [n_splits][B*H][Lq][d]
   float *part_ml;  // split-KV row stats        [n_splits][B*H][Lq][2] (log2 max, sum)
+  const void *colc; // DeBERTa per-key constants [B*H][Lk] x 8 bytes (relattn_colc_kernel)
   int32_t B, H, Lq, Lk;
   int32_t q_pos_offset, causal;
   int32_t clip_k;
@@ -54,6 +55,12 @@ struct IndexArgs {
   int32_t kind, which, clip_k;
   int32_t t5_slots, t5_exact, t5_bidir, t5_nthr;
   int32_t t5_thr[kT5MaxThr];  // entries from t5_nthr on hold INT32_MAX
+};
+
+struct ColcArgs {
+  const void *k, *qr;
+  void *colc;
+  int32_t BH, H, Lk, clip_k;
 };
 
 struct CombineArgs {

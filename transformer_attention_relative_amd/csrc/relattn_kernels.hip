@@ -243,17 +243,6 @@ struct TableFrag<true, D> {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) v[t] = {};
   }
-  // x + y, rounded once to bfloat16 (nearest even)
-  __device__ __forceinline__ void sum_of(const TableFrag& x, const TableFrag& y) {
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 z = cvt2((float)x.v[t][e] + (float)y.v[t][e], (float)x.v[t][e + 1] + (float)y.v[t][e + 1]);
-        v[t][e] = z[0];
-        v[t][e + 1] = z[1];
-      }
-  }
 };
 template <int D>
 struct TableFrag<false, D> {
@@ -275,10 +264,6 @@ struct TableFrag<false, D> {
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int t = 0; t < D / 2; ++t) v[t] = 0.f;
-  }
-  __device__ __forceinline__ void sum_of(const TableFrag& x, const TableFrag& y) {
-#pragma unroll
-    for (int t = 0; t < D / 2; ++t) v[t] = x.v[t] + y.v[t];
   }
 };
 
@@ -460,6 +445,42 @@ __device__ __forceinline__ float ref_offset(float cb, float m_ref) {
   return m_ref == RA_NEG_INF ? 0x1p100f : cb - m_ref;
 }
 
+// DeBERTa blocks whose offsets are all clipped use one Qr row for every pair,
+// so their position-to-content term k_j.Qr[d] is a per-key constant.  The
+// constants come from relattn_colc_kernel (float32 dot products) and enter
+// the score accumulator through one MFMA: A holds the key's constants (as
+// bfloat16 hi + lo pairs, or float32), B selects the side for every query.
+template <bool BF>
+struct KeyConst;
+template <>
+struct KeyConst<true> {
+  bf16x8 v;  // lanes of half 0: {hi0, lo0, hi1, lo1, 0, 0, 0, 0} of key lq
+  __device__ __forceinline__ void load(const void* colc, size_t base, int key, int hh) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(colc) + (base + key) * 4);
+    const bf16 z = (bf16)0.f;
+    v = hh == 0 ? bf16x8{x[0], x[1], x[2], x[3], z, z, z, z} : bf16x8{};
+  }
+};
+template <>
+struct KeyConst<false> {
+  float v;  // k-slot hh: the key's side-hh constant
+  __device__ __forceinline__ void load(const void* colc, size_t base, int key, int hh) {
+    v = reinterpret_cast<const float*>(colc)[(base + key) * 2 + hh];
+  }
+};
+
+template <bool BF>
+__device__ __forceinline__ f32x16 mma_keyconst(const KeyConst<BF>& kc, int side, int hh) {
+  if constexpr (BF) {
+    const bf16 one = (bf16)1.f, z = (bf16)0.f;
+    bf16x8 sel = {};
+    if (hh == 0) sel = side == 0 ? bf16x8{one, one, z, z, z, z, z, z} : bf16x8{z, z, one, one, z, z, z, z};
+    return mma_bf16(kc.v, sel, f32x16{});
+  } else {
+    return mma_f32(kc.v, hh == side ? 1.f : 0.f, f32x16{});
+  }
+}
+
 template <int KIND, bool BF, int D, int QB, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a) {
   static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
@@ -523,26 +544,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   // copy is issued: a wait for any of them then never waits for a tile ------
   const int kv_valid = a.kv_valid_len ? __builtin_amdgcn_readfirstlane(a.kv_valid_len[b]) : a.Lk;
   QFrag qf[QB];
-  // DeBERTa: q + Qr[0] and q + Qr[2k-1] (rounded once to the input type).
-  // Where every offset of a block is clipped, q.k + k.Qr[d(j,i)] equals
-  // (q + Qr[d]).k with a single Qr row, so the position-to-content term of
-  // such blocks rides on the content MFMA.
-  QFrag qside[KIND == 2 ? QB : 1][KIND == 2 ? 2 : 1];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (qrow[qb] < a.Lq) qf[qb].load(Qg + (size_t)qrow[qb] * D, hh);
     else qf[qb].zero();
-  }
-  if constexpr (KIND == 2) {
-    const T* qr = reinterpret_cast<const T*>(a.table2);
-    QFrag r0, r1;
-    r0.load(qr + (size_t)h * D, hh);
-    r1.load(qr + ((size_t)(2 * ck - 1) * a.H + h) * D, hh);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      qside[qb][0].sum_of(qf[qb], r0);
-      qside[qb][1].sum_of(qf[qb], r1);
-    }
   }
   constexpr int LUT_EARLY = 8;  // offset-table entries per thread fetched early
   float lut_early[LUT_EARLY];
@@ -800,6 +805,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         else if (-omin <= -ck) { deb_side[qb] = 1; b_tile[qb] = crow_lo[qb]; } // every query - key <= -k
       }
     }
+    // DeBERTa: the per-key constants of the tile's keys (for clipped blocks)
+    KeyConst<BF> kc[KIND == 2 ? NKB : 1];
+    if constexpr (KIND == 2) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kc[kb].load(a.colc, (size_t)bh * a.Lk, min(k0 + 32 * kb + lq, a.Lk - 1), hh);
+    }
     // exponent offsets c*b - m_ref of the tile's blocks
     float off[QB];
 #pragma unroll
@@ -862,7 +873,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         } else {
           const int side = CLS == 0 ? deb_side[qb] : deb_block_side(qb);
           if (side >= 0) {
-            s = mma_frag0<BF, D>(kf, side == 0 ? qside[qb][0] : qside[qb][1]);
+            // k_j.Qr[0] (side 0) or k_j.Qr[2k-1] (side 1) for every query
+            s = mma_keyconst<BF>(kc[kb], side, hh);
+            s = mma_frag<BF, D>(kf, qf[qb], s);
           } else {
             float* cband = relf + wave * L.deb_wave_floats;
             float* pband = cband + kBlockRows * kCbandStride;
@@ -1217,6 +1230,45 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
   }
 }
 
+// DeBERTa per-key constants: k_j.Qr[0][h] and k_j.Qr[2k-1][h] in float32, for
+// blocks whose offsets are all clipped (key far before / far after the
+// query).  bfloat16 inputs store each as hi + lo bfloat16 ({hi0, lo0, hi1,
+// lo1} per key); float32 inputs store the pair.  Reads K once.
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
+  using T = typename std::conditional<BF, bf16, float>::type;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.BH * a.Lk) return;
+  const int bh = (int)(idx / a.Lk);
+  const int h = bh % a.H;
+  const T* kr = reinterpret_cast<const T*>(a.k) + idx * D;
+  const T* q0 = reinterpret_cast<const T*>(a.qr) + (size_t)h * D;
+  const T* q1 = reinterpret_cast<const T*>(a.qr) + ((size_t)(2 * a.clip_k - 1) * a.H + h) * D;
+  float s0 = 0.f, s1 = 0.f;
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte load
+#pragma unroll
+  for (int t = 0; t < D / EPV; ++t) {
+    const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + EPV * t);
+    const f32x4 ax = *reinterpret_cast<const f32x4*>(q0 + EPV * t);
+    const f32x4 bx = *reinterpret_cast<const f32x4*>(q1 + EPV * t);
+    const T* ke = reinterpret_cast<const T*>(&kx);
+    const T* ae = reinterpret_cast<const T*>(&ax);
+    const T* be = reinterpret_cast<const T*>(&bx);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      s0 = fmaf((float)ke[e], (float)ae[e], s0);
+      s1 = fmaf((float)ke[e], (float)be[e], s1);
+    }
+  }
+  if constexpr (BF) {
+    const bf16 h0 = (bf16)s0, h1 = (bf16)s1;
+    const bf16x4 y = {h0, (bf16)(s0 - (float)h0), h1, (bf16)(s1 - (float)h1)};
+    reinterpret_cast<bf16x4*>(a.colc)[idx] = y;
+  } else {
+    reinterpret_cast<f32x2*>(a.colc)[idx] = f32x2{s0, s1};
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Host-side launch helpers (called from relattn_api.cpp)
 // ----------------------------------------------------------------------------
@@ -1261,6 +1313,16 @@ hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) 
   else if (bf && d == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
   else if (!bf && d == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st) {
+  const int64_t threads = (int64_t)a.BH * a.Lk;
+  const int grid = (int)((threads + 255) / 256);
+  if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
+  else if (bf && d == 32) hipLaunchKernelGGL((relattn_colc_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
+  else if (!bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((relattn_colc_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
