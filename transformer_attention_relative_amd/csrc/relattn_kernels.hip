@@ -539,9 +539,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   const int wg_pos_max = a.q_pos_offset + min(q0 + BQ, a.Lq) - 1;
   const int ck = a.clip_k;
 
-  // ---- register loads first (valid length, Q fragments, the kind's small
-  // tables), all consumed by the prologue before the first key/value tile
-  // copy is issued: a wait for any of them then never waits for a tile ------
+  // ---- the first key/value tile copies go out before anything else when
+  // their keys are known at launch (no per-sequence valid length, or an
+  // unsplit key range, which starts at key 0), so they overlap every load of
+  // the prologue.  Tiles past a short valid length are read for nothing and
+  // never used (the loop's in-order waits only wait longer).  A split key
+  // range under a valid length starts at a tile that depends on it, so its
+  // first copies wait for it.
+  const int causal_end = a.causal ? min(a.Lk, wg_pos_max + 1) : a.Lk;
+  const bool early_copies = a.n_splits == 1 || a.kv_valid_len == nullptr;
+  if (early_copies) {
+    const int n_kt0 = (causal_end + kBK - 1) / kBK;
+    const int per0 = (n_kt0 + a.n_splits - 1) / a.n_splits;
+    const int beg0 = min(n_kt0, split * per0);
+    const int n0 = min(n_kt0, beg0 + per0) - beg0;
+    Dma dma;
+    dma.init(wave, lane);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < n0) dma.issue(Kg, Vg, a.Lk, (beg0 + s) * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
+  }
+
+  // ---- register loads (valid length, Q fragments, the kind's small tables)
   const int kv_valid = a.kv_valid_len ? __builtin_amdgcn_readfirstlane(a.kv_valid_len[b]) : a.Lk;
   QFrag qf[QB];
 #pragma unroll
@@ -549,7 +568,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     if (qrow[qb] < a.Lq) qf[qb].load(Qg + (size_t)qrow[qb] * D, hh);
     else qf[qb].zero();
   }
-  constexpr int LUT_EARLY = 8;  // offset-table entries per thread fetched early
+  // T5: distinct offset-table entries per thread fetched early (the table
+  // holds lut_stride + 3 distinct offsets; 4 x 64 x NW covers 2048 of them
+  // with 8 waves, 1024 with 4)
+  constexpr int LUT_EARLY = 4;
   float lut_early[LUT_EARLY];
   float bias_left = 0.f, bias_right = 0.f;          // T5 saturated buckets / scale
   constexpr int SHAW_RB = 3;                          // blocks of 32 a_K rows (k <= 32)
@@ -560,14 +582,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     const float* tab = reinterpret_cast<const float*>(a.table);
 #pragma unroll
     for (int i = 0; i < LUT_EARLY; ++i) {
-      const int e = tid + i * 64 * NW;
+      const int x = tid + i * 64 * NW;
       lut_early[i] = 0.f;
-      if (e < 4 * L.lut_stride) {
-        const int cpy = e / L.lut_stride, x = e - cpy * L.lut_stride + cpy;
-        if (x < a.lut_n) {
-          const int bk = t5_bucket_dev(a.lut_lo + x, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
-          lut_early[i] = tab[bk * a.H + h];
-        }
+      if (x < a.lut_n) {
+        const int bk = t5_bucket_dev(a.lut_lo + x, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
+        lut_early[i] = tab[bk * a.H + h];
       }
     }
     const int bl = t5_bucket_dev(-(1 << 30), a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
@@ -601,7 +620,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   }
 
   const int kv_lim = max(0, min(a.Lk, kv_valid));
-  const int kv_end = a.causal ? min(kv_lim, wg_pos_max + 1) : kv_lim;
+  const int kv_end = min(kv_lim, causal_end);
   const int n_kt = kv_end > 0 ? (kv_end + kBK - 1) / kBK : 0;
   const int per_split = (n_kt + a.n_splits - 1) / a.n_splits;
   const int kt_begin = min(n_kt, split * per_split);
@@ -616,22 +635,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = crow_lo[qb] = crow_hi[qb] = 0.f;
 
   if constexpr (KIND == 0) {
-    // four copies of bias[offset]/scale, copy c shifted by c entries
+    // four copies of bias[offset]/scale, copy c shifted by c entries:
+    // entry x of the table goes to copy c at position x - c
     const float inv_scale = 1.f / a.scale;
+    const int nx = L.lut_stride + 3;
+    auto put4 = [&](const int x, const float val) {
+#pragma unroll
+      for (int cpy = 0; cpy < 4; ++cpy) {
+        const int y = x - cpy;
+        if (y >= 0 && y < L.lut_stride) relf[cpy * L.lut_stride + y] = val;
+      }
+    };
 #pragma unroll
     for (int i = 0; i < LUT_EARLY; ++i) {
-      const int e = tid + i * 64 * NW;
-      if (e < 4 * L.lut_stride) relf[e] = lut_early[i] * inv_scale;
+      const int x = tid + i * 64 * NW;
+      if (x < nx) put4(x, lut_early[i] * inv_scale);
     }
     const float* tab = reinterpret_cast<const float*>(a.table);
-    for (int e = tid + LUT_EARLY * 64 * NW; e < 4 * L.lut_stride; e += 64 * NW) {
-      const int cpy = e / L.lut_stride, x = e - cpy * L.lut_stride + cpy;
+    for (int x = tid + LUT_EARLY * 64 * NW; x < nx; x += 64 * NW) {
       float val = 0.f;
       if (x < a.lut_n) {
         const int bk = t5_bucket_dev(a.lut_lo + x, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
         val = tab[bk * a.H + h] * inv_scale;
       }
-      relf[e] = val;
+      put4(x, val);
     }
   } else if constexpr (KIND == 1) {
     // arel[row][r] = q.a_K[r] - q.a_K[0], r = 0..2k, by MFMA over blocks of
@@ -682,8 +709,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     }
   }
 
-  // ---- start streaming the first key tiles --------------------------------
-  {
+  // ---- start streaming the first key tiles of a split key range ------------
+  if (!early_copies) {
     Dma dma;
     dma.init(wave, lane);
 #pragma unroll
