@@ -909,12 +909,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
             const T* kr = reinterpret_cast<const T*>(a.table);
             const T* qr = reinterpret_cast<const T*>(a.table2);
             const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
+            // the four table fragments of the block's two bands are requested
+            // together, so their L2 latencies overlap instead of adding up
+            TableFrag<BF, D> af[2], bfr[2];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+              af[tb].load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              bfr[nb].load(qr + ((size_t)deberta_delta_dev(-(T0 + 32 * nb + lq), ck) * a.H + h) * D, hh);
             // content-to-position: rows Kr[delta(T0 + m)], columns = queries
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-              TableFrag<BF, D> af;
-              af.load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
-              const f32x16 acc = mma_frag0<BF, D>(af, qf[qb]);
+              const f32x16 acc = mma_frag0<BF, D>(af[tb], qf[qb]);
               float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
@@ -927,9 +934,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
               const int n = 32 * nb + lq;
-              TableFrag<BF, D> bfr;
-              bfr.load(qr + ((size_t)deberta_delta_dev(-(T0 + n), ck) * a.H + h) * D, hh);
-              const f32x16 acc = mma_frag0<BF, D>(kf, bfr);
+              const f32x16 acc = mma_frag0<BF, D>(kf, bfr[nb]);
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int jl = acc_row(i, hh);
