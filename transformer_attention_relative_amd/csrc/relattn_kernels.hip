@@ -1227,7 +1227,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 
 // Merge split-KV partials: each split holds an unnormalised output and its
 // (max, sum) in the exp2 domain; rescale to the common max and normalise.
-template <bool BF, int D>
+// One thread per 4 output elements of a row; the (max, sum) pairs and the
+// output chunks of every split are requested together (MS splits at most,
+// MS a multiple of 4), so the merge costs one memory round trip.
+template <bool BF, int D, int MS>
 __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
   using T = typename std::conditional<BF, bf16, float>::type;
   const int64_t nrow = (int64_t)a.BH * a.Lq;
@@ -1235,19 +1238,31 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
   const int64_t row = idx / (D / 4);
   const int ch = (int)(idx % (D / 4));
   if (row >= nrow) return;
+  f32x2 ml[MS];
+  f32x4 po[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (s < a.n_splits) {
+      const size_t r = (size_t)s * nrow + row;
+      ml[s] = *reinterpret_cast<const f32x2*>(a.part_ml + r * 2);
+      po[s] = *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * ch);
+    } else {
+      ml[s] = f32x2{RA_NEG_INF, 0.f};
+      po[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   float M = RA_NEG_INF;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_ml[((size_t)s * nrow + row) * 2]);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) M = fmaxf(M, ml[s][0]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float Lsum = 0.f;
   if (M != RA_NEG_INF) {
-    for (int s = 0; s < a.n_splits; ++s) {
-      const size_t r = (size_t)s * nrow + row;
-      const float ms = a.part_ml[r * 2], ls = a.part_ml[r * 2 + 1];
-      if (!(ls > 0.f)) continue;
-      const float w = fast_exp2(ms - M);
-      Lsum += w * ls;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * ch);
-      acc += w * x;
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      // splits that saw no visible key hold (-inf, 0): weight 0
+      const float w = ml[s][1] > 0.f ? fast_exp2(ml[s][0] - M) : 0.f;
+      Lsum += w * ml[s][1];
+      acc += w * po[s];
     }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
@@ -1338,13 +1353,20 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
   return hipErrorInvalidValue;
 }
 
+template <bool BF, int D>
+static void launch_combine_t(const CombineArgs& a, int grid, hipStream_t st) {
+  if (a.n_splits <= 8) hipLaunchKernelGGL((relattn_combine_kernel<BF, D, 8>), dim3(grid), dim3(256), 0, st, a);
+  else if (a.n_splits <= 16) hipLaunchKernelGGL((relattn_combine_kernel<BF, D, 16>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((relattn_combine_kernel<BF, D, kMaxSplits>), dim3(grid), dim3(256), 0, st, a);
+}
+
 hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) {
   const int64_t threads = (int64_t)a.BH * a.Lq * (d / 4);
   const int grid = (int)((threads + 255) / 256);
-  if (bf && d == 64) hipLaunchKernelGGL((relattn_combine_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
-  else if (bf && d == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
-  else if (!bf && d == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);
+  if (bf && d == 64) launch_combine_t<true, 64>(a, grid, st);
+  else if (bf && d == 32) launch_combine_t<true, 32>(a, grid, st);
+  else if (!bf && d == 64) launch_combine_t<false, 64>(a, grid, st);
+  else launch_combine_t<false, 32>(a, grid, st);
   return hipGetLastError();
 }
 
