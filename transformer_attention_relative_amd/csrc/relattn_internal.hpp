@@ -81,6 +81,13 @@ RELATTN_HD constexpr int num_stages(int kind, bool bf16) { return kind == 0 ? (b
 // whole MFMA contraction chunks.
 RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k - 1) + 15) / 16 * 16; }
 
+// Row stride (elements) of the Shaw bin rows in LDS: the slots plus 16 bytes,
+// an odd multiple of 16 bytes, so that the per-lane bin stores of the 32
+// rows of a block spread over 16 bank groups instead of 4.
+RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
+  return shaw_bin_slots(clip_k) + (((shaw_bin_slots(clip_k) * esz / 16) % 2 == 0) ? 16 / esz : 0);
+}
+
 // ---- LDS layout ------------------------------------------------------------
 // Stage s holds the K tile then the V tile of one key tile, each kBK rows of
 // d elements, row-major; 16-byte chunks are XOR-swizzled within a row
@@ -89,8 +96,10 @@ RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k - 1) +
 //   T5      float lut4[4][lut_stride]: four copies of bias[offset]*log2(e),
 //           copy c shifted by c entries, so any 4 consecutive offsets are one
 //           aligned 16-byte read
-//   SHAW    per wave: float arel[rows][2k+1]; per wave: bin scratch
-//           [32][bin_slots] (input dtype); bf16 only: a_V^T [d][bin_slots]
+//   SHAW    per wave: arel[rows][2k+2] (input dtype: q.a_K[r] - q.a_K[0]);
+//           per wave: float r2k[rows] (the r = 2k entry, unrounded); per
+//           wave: bin rows [rows][bin_slots] (input dtype), one per query
+//           row of the wave; bf16 only: a_V^T [d][bin_slots]
 //   DEBERTA per wave: float cband[32][kCbandStride], float pband[32][kPbandStride]
 constexpr int kCbandStride = 68;  // 63 band rows, padded so that rows hit distinct banks
 constexpr int kPbandStride = 36;  // 32 keys, padded; rows stay 16-byte aligned
@@ -98,7 +107,7 @@ constexpr int kPbandStride = 36;  // 32 keys, padded; rows stay 16-byte aligned
 struct LdsLayout {
   int stage_bytes, tile_bytes, rel_off, total;
   int lut_stride;
-  int arel_stride, arel_wave_floats, wscr_off, wscr_wave_bytes, avt_off;
+  int arel_stride, arel_wave_bytes, r2k_off, wscr_off, wscr_wave_bytes, avt_off;
   int deb_wave_floats;
 };
 
@@ -120,10 +129,10 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     const int nbin = shaw_bin_slots(clip_k);
     // even stride: a row read at offset (const - row) walks 33 banks per row
     L.arel_stride = 2 * clip_k + 2;
-    L.arel_wave_floats = rows * L.arel_stride;
-    const int arel_bytes = (nw * L.arel_wave_floats * 4 + 15) / 16 * 16;
-    L.wscr_off = arel_bytes;
-    L.wscr_wave_bytes = kBlockRows * nbin * esz;
+    L.arel_wave_bytes = (rows * L.arel_stride * esz + 15) / 16 * 16;
+    L.r2k_off = nw * L.arel_wave_bytes;
+    L.wscr_off = L.r2k_off + nw * rows * 4;
+    L.wscr_wave_bytes = rows * shaw_bin_stride(clip_k, esz) * esz;
     L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
     rel_bytes = L.avt_off + (bf16 ? d * nbin * 2 : 0);
   } else {

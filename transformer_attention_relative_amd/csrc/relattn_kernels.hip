@@ -630,7 +630,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   // ---- per-kind prologue (LDS tables) ---------------------------------------
   float shaw_right[QB];                              // Shaw: q.(a_K[2k] - a_K[0])
   float crow_lo[QB], crow_hi[QB];                    // DeBERTa: q.Kr[0], q.Kr[2k-1]
-  float* arel = nullptr;
+  T* arel = nullptr;     // Shaw: this wave's relative-key logits (input dtype)
+  T* wbins = nullptr;    // Shaw: this wave's bin rows, [32 * QB][bin slots]
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = crow_lo[qb] = crow_hi[qb] = 0.f;
 
@@ -664,7 +665,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     // arel[row][r] = q.a_K[r] - q.a_K[0], r = 0..2k, by MFMA over blocks of
     // 32 table rows; subtracting the r = 0 value is softmax-neutral and
     // makes every key beyond -k contribute exactly zero.
-    arel = relf + wave * L.arel_wave_floats;
+    arel = reinterpret_cast<T*>(smem + L.rel_off + wave * L.arel_wave_bytes);
+    float* r2k = reinterpret_cast<float*>(smem + L.rel_off + L.r2k_off) + wave * 32 * QB;
+    wbins = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes);
     const int nrow = 2 * ck + 1;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -678,13 +681,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = min(rb * 32 + acc_row(i, hh), nrow);
-          arel[(32 * qb + lq) * L.arel_stride + r] = acc[i] - base0;
+          arel[(32 * qb + lq) * L.arel_stride + r] = (T)(acc[i] - base0);
+          if (r == 2 * ck) r2k[32 * qb + lq] = acc[i] - base0;  // kept unrounded
         }
+      }
+    }
+    // bin rows start (and are kept) at zero; this lane clears its half of
+    // each of its rows
+    {
+      const int nbin = shaw_bin_slots(ck);
+      constexpr int EPV = 16 / sizeof(T);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x4* zp = reinterpret_cast<f32x4*>(wbins + (32 * qb + lq) * shaw_bin_stride(ck, (int)sizeof(T)) + hh * (nbin / 2));
+        for (int x = 0; x < nbin / 2 / EPV; ++x) zp[x] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     wave_lds_fence();
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = arel[(32 * qb + lq) * L.arel_stride + 2 * ck];
+    for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = r2k[32 * qb + lq];
     if constexpr (BF) {
       // a_V^T for the in-window bins: avt[d][r'] = a_V[r' + 1][d], r' < 2k - 1
       const int nb = shaw_bin_slots(ck);
@@ -734,6 +749,50 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     lr_run[qb] = 0.f;        // Shaw: partial mass of keys at offset >= k
     win_run[qb] = 0.f;       // Shaw: partial mass of keys inside the clip window
   }
+
+  // Shaw: apply the pending bins of query block qb (o += a_V^T W^T), then
+  // clear them.  Wave-uniform; a no-op when no bin was written since the
+  // last flush.
+  bool bins_dirty[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) bins_dirty[qb] = false;
+  auto flush_bins = [&](const int qb) {
+    if constexpr (KIND == 1) {
+      if (!bins_dirty[qb]) return;
+      bins_dirty[qb] = false;
+      const int ln = opaque_lane();
+      const int lq = ln & 31, hh = ln >> 5;
+      const int nbin = shaw_bin_slots(ck);
+      T* wrow = wbins + (32 * qb + lq) * shaw_bin_stride(ck, (int)sizeof(T));
+      wave_lds_fence();
+      if constexpr (BF) {
+        const bf16* avt = reinterpret_cast<const bf16*>(smem + L.rel_off + L.avt_off);
+        for (int cb = 0; cb < nbin / 16; ++cb) {
+          const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 16 * cb + 8 * hh);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(avt + (32 * db + lq) * nbin + 16 * cb + 8 * hh);
+            o[qb][db] = mma_bf16(vf, wf, o[qb][db]);
+          }
+        }
+      } else {
+        const float* av = reinterpret_cast<const float*>(a.table2);
+        for (int cb = 0; cb < nbin / 2; ++cb) {
+          const int rr = 2 * cb + hh;
+          const float wv = wrow[rr];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const float vv = rr < 2 * ck - 1 ? av[(size_t)(rr + 1) * D + 32 * db + lq] : 0.f;
+            o[qb][db] = mma_f32(vv, wv, o[qb][db]);
+          }
+        }
+      }
+      wave_lds_fence();
+      constexpr int EPV = 16 / sizeof(T);
+      f32x4* zp = reinterpret_cast<f32x4*>(wrow + hh * (nbin / 2));
+      for (int x = 0; x < nbin / 2 / EPV; ++x) zp[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
 
   // Tile classes (wave-uniform):
   //   0: every block far from the diagonal band (the relative term is a
@@ -888,11 +947,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
           }
         } else if constexpr (KIND == 1) {
           if (CLS == 2 && near[qb]) {
-            const float* ar = arel + (32 * qb + lq) * L.arel_stride;
+            const T* ar = arel + (32 * qb + lq) * L.arel_stride;
             const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
             f32x16 init;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) init[i] = ar[shaw_row_dev(obase + acc_row(i, 0), ck)];
+            for (int i = 0; i < 16; ++i) init[i] = (float)ar[shaw_row_dev(obase + acc_row(i, 0), ck)];
             s = mma_frag<BF, D>(kf, qf[qb], init);
           } else {
             s = mma_frag0<BF, D>(kf, qf[qb]);
@@ -1031,6 +1090,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
           for (int i = 0; i < 16; ++i) s[qb][i] = fmaf(s[qb][i], c, cb);
           const float mn = fmaxf(m_ref[qb], max_halves(max16(s[qb])));
           const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m_ref[qb] - mn);
+          if constexpr (KIND == 1) flush_bins(qb);  // bins hold p at the old reference
 #pragma unroll
           for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
           l_run[qb] *= alpha;
@@ -1054,15 +1114,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
           if (far_right[qb]) {
             lr_run[qb] += lsum[qb];
           } else if (CLS == 2 && near[qb]) {
+            // keys inside the window: their probability goes to the row's
+            // own bin (each offset belongs to exactly one key of a row, so a
+            // bin is assigned once); the bins are multiplied by a_V when the
+            // row is done or before its running state is rescaled
             const int nbin = shaw_bin_slots(ck);
-            T* wrow = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes) + lq * nbin;
-            {
-              // this lane clears its half of the row: nbin/2 elements, 16-byte stores
-              constexpr int EPV = 16 / sizeof(T);
-              f32x4* zp = reinterpret_cast<f32x4*>(wrow + hh * (nbin / 2));
-              for (int x = 0; x < nbin / 2 / EPV; ++x) zp[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            wave_lds_fence();
+            T* wrow = wbins + (32 * qb + lq) * shaw_bin_stride(ck, (int)sizeof(T));
+            // Branch-free: keys outside the window store to the row's last
+            // slot, a padding slot (2k - 1 < bin slots) that meets a zero
+            // a_V^T row in the bin product.
             float win = 0.f, lr = 0.f;
             const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
 #pragma unroll
@@ -1071,39 +1131,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
               float pv;
               if constexpr (BF) pv = (float)pf[qb][i >> 3][i & 7];
               else pv = s[qb][i];
-              if (offk > -ck && offk < ck) {
-                wrow[offk + ck - 1] = (T)pv;
-                win += pv;
-              } else if (offk >= ck) {
-                lr += pv;
-              }
+              const bool in_win = offk > -ck && offk < ck;
+              wrow[in_win ? offk + ck - 1 : nbin - 1] = (T)pv;
+              win += in_win ? pv : 0.f;
+              lr += offk >= ck ? pv : 0.f;
             }
             win_run[qb] += win;
             lr_run[qb] += lr;
-            wave_lds_fence();
-            if constexpr (BF) {
-              const bf16* avt = reinterpret_cast<const bf16*>(smem + L.rel_off + L.avt_off);
-              for (int cb = 0; cb < nbin / 16; ++cb) {
-                const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 16 * cb + 8 * hh);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                  const bf16x8 vf = *reinterpret_cast<const bf16x8*>(avt + (32 * db + lq) * nbin + 16 * cb + 8 * hh);
-                  o[qb][db] = mma_bf16(vf, wf, o[qb][db]);
-                }
-              }
-            } else {
-              const float* av = reinterpret_cast<const float*>(a.table2);
-              for (int cb = 0; cb < nbin / 2; ++cb) {
-                const int rr = 2 * cb + hh;
-                const float wv = wrow[rr];
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                  const float vv = rr < 2 * ck - 1 ? av[(size_t)(rr + 1) * D + 32 * db + lq] : 0.f;
-                  o[qb][db] = mma_f32(vv, wv, o[qb][db]);
-                }
-              }
-            }
-            wave_lds_fence();  // the next near block rewrites the bin tile
+            bins_dirty[qb] = true;
           }
         }
       }
@@ -1173,6 +1208,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
     if constexpr (KIND == 1) {
+      flush_bins(qb);
       // bins 0 and 2k take the row mass not held by the in-window bins
       const T* av = reinterpret_cast<const T*>(a.table2);
       const float lr_tot = lr_run[qb] + __shfl_xor(lr_run[qb], 32);
