@@ -1068,6 +1068,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
           s[qb] = scores(qb, kf);
         }
       }
+      // One query block per wave leaves registers to spare: the V^T
+      // fragments of the step are read before the softmax, so their LDS
+      // latency hides behind it instead of sitting between it and P V.
+      constexpr bool EARLY_V = BF && QB == 1;
+      bf16x8 vpre[EARLY_V ? 2 : 1][EARLY_V ? NDB : 1];
+      if constexpr (EARLY_V) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) vpre[h2][db] = load_vt_frag<D>(vtile, 2 * kb + h2, ko.v[db]);
+      }
       bool bad = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -1149,7 +1160,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const bf16x8 vf = load_vt_frag<D>(vtile, 2 * kb + h2, ko.v[db]);
+            bf16x8 vf;
+            if constexpr (EARLY_V) vf = vpre[h2][db];
+            else vf = load_vt_frag<D>(vtile, 2 * kb + h2, ko.v[db]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               if ((QM >> qb) & 1) o[qb][db] = mma_bf16(vf, pf[qb][h2], o[qb][db]);
