@@ -100,9 +100,10 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //           per wave: float r2k[rows] (the r = 2k entry, unrounded); per
 //           wave: bin rows [rows][bin_slots] (input dtype), one per query
 //           row of the wave; bf16 only: a_V^T [d][bin_slots]
-//   DEBERTA per wave: float cband[32][kCbandStride], float pband[32][kPbandStride]
-constexpr int kCbandStride = 68;  // 63 band rows, padded so that rows hit distinct banks
-constexpr int kPbandStride = 36;  // 32 keys, padded; rows stay 16-byte aligned
+//   DEBERTA per wave: float band[32][kCbandStride], the content-to-position
+//           band [query][m] and then the position-to-content band [key][n]
+constexpr int kCbandStride = 68;  // 64 band columns, padded: rows stay 16-byte aligned and
+                                  // a query's diagonal (stride 69) hits distinct banks
 
 struct LdsLayout {
   int stage_bytes, tile_bytes, rel_off, total;
@@ -136,7 +137,7 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
     rel_bytes = L.avt_off + (bf16 ? d * nbin * 2 : 0);
   } else {
-    L.deb_wave_floats = kBlockRows * kCbandStride + kBlockRows * kPbandStride;
+    L.deb_wave_floats = kBlockRows * kCbandStride;
     rel_bytes = nw * L.deb_wave_floats * 4;
   }
   L.total = L.rel_off + ((rel_bytes + 15) & ~15);

@@ -963,11 +963,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
             s = mma_keyconst<BF>(kc[kb], side, hh);
             s = mma_frag<BF, D>(kf, qf[qb], s);
           } else {
-            float* cband = relf + wave * L.deb_wave_floats;
-            float* pband = cband + kBlockRows * kCbandStride;
+            // one 32 x kCbandStride float tile per wave, used first for the
+            // content-to-position band, then for the position-to-content band
+            float* band = relf + wave * L.deb_wave_floats;
             const T* kr = reinterpret_cast<const T*>(a.table);
             const T* qr = reinterpret_cast<const T*>(a.table2);
-            const int T0 = pq_min - j0 - 31;  // band row m <-> query - key = T0 + m
+            const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
             // the four table fragments of the block's two bands are requested
             // together, so their L2 latencies overlap instead of adding up
             TableFrag<BF, D> af[2], bfr[2];
@@ -977,41 +978,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
               bfr[nb].load(qr + ((size_t)deberta_delta_dev(-(T0 + 32 * nb + lq), ck) * a.H + h) * D, hh);
-            // content-to-position: rows Kr[delta(T0 + m)], columns = queries
+            // content-to-position: rows Kr[delta(T0 + m)], columns = queries,
+            // stored [query][m]
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
               const f32x16 acc = mma_frag0<BF, D>(af[tb], qf[qb]);
-              float* dst = cband + lq * kCbandStride + 32 * tb + 4 * hh;
+              float* dst = band + lq * kCbandStride + 32 * tb + 4 * hh;
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
                 const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
                 *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
               }
             }
+            wave_lds_fence();
+            // key j0 + jl of query row lq sits at m = lq - jl + 31
+            float cg[16];
+            {
+              const float* crow = band + lq * (kCbandStride + 1) + 31;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) cg[i] = crow[-acc_row(i, hh)];
+            }
             // position-to-content: rows = keys, columns n <-> query - key =
-            // T0 + n, Qr row delta(key - query); scattered to [query][key]
+            // T0 + n, Qr row delta(key - query); stored [key][n] over the
+            // same tile (the reads above precede these writes in the wave's
+            // LDS order): every address is a lane base plus a constant
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-              const int n = 32 * nb + lq;
               const f32x16 acc = mma_frag0<BF, D>(kf, bfr[nb]);
+              float* dst = band + 32 * nb + lq;
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int jl = acc_row(i, hh);
-                const int sq = n + jl - 31;
-                if (sq >= 0 && sq < 32) pband[sq * kPbandStride + jl] = acc[i];
-              }
+              for (int i = 0; i < 16; ++i) dst[acc_row(i, hh) * kCbandStride] = acc[i];
             }
             wave_lds_fence();
-            const float* crow = cband + lq * kCbandStride + (pos[qb] - pq_min) + 31;
-            const float* prow = pband + lq * kPbandStride;
+            // key j0 + jl of query row lq sits at n = lq - jl + 31
             f32x16 init;
+            {
+              const float* prow = band + lq + 31;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 pc = *reinterpret_cast<const f32x4*>(prow + 8 * g + 4 * hh);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) init[4 * g + e] = crow[-(8 * g + 4 * hh + e)] + pc[e];
+              for (int i = 0; i < 16; ++i) init[i] = cg[i] + prow[acc_row(i, hh) * (kCbandStride - 1)];
             }
-            wave_lds_fence();  // the next block overwrites both bands
+            wave_lds_fence();  // the next block overwrites the tile
             s = mma_frag<BF, D>(kf, qf[qb], init);
           }
         }
