@@ -142,8 +142,8 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   const float dflt = p->kind == RELATTN_DEBERTA ? 1.f / std::sqrt(3.f * p->d) : 1.f / std::sqrt((float)p->d);
   P->scale = p->scale > 0.f ? p->scale : dflt;
 
-  // Kernel variant.  DeBERTa: 8 waves x 32 rows in bfloat16 (its near-block
-  // bands need 13 KiB of LDS per wave), 4 waves in float32.  T5 / Shaw: 4 waves; 64 rows per wave when there
+  // Kernel variant: 4 waves.  DeBERTa: 32 rows per wave (its near-block band
+  // tile takes 8.5 KiB of LDS per wave; two workgroups fit a CU).  T5 / Shaw: 64 rows per wave when there
   // are enough workgroups to fill two per CU (one LDS fragment then feeds two
   // MFMAs) and the LDS fits two workgroups per CU, else 32 rows per wave.
   // float32 always uses 32 rows per wave (its fragments are twice as large).
@@ -162,7 +162,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     *total = lds_layout(p->kind, P->bf, p->d, v.qb, v.nw, p->clip_k, *lut_n).total;
     return RELATTN_OK;
   };
-  Variant var = (p->kind == RELATTN_DEBERTA && P->bf) ? Variant{8, 1} : Variant{4, 1};
+  Variant var = Variant{4, 1};
   int lds_total = 0, lut_n = 0;
   if (p->kind != RELATTN_DEBERTA && P->bf) {
     const int64_t wgs2 = (int64_t)BH * ((p->Lq + 4 * 64 - 1) / (4 * 64));

@@ -569,8 +569,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     else qf[qb].zero();
   }
   // T5: distinct offset-table entries per thread fetched early (the table
-  // holds lut_stride + 3 distinct offsets; 4 x 64 x NW covers 2048 of them
-  // with 8 waves, 1024 with 4)
+  // holds lut_stride + 3 distinct offsets; 4 x 64 x NW covers 1024 of them
+  // with 4 waves)
   constexpr int LUT_EARLY = 4;
   float lut_early[LUT_EARLY];
   float bias_left = 0.f, bias_right = 0.f;          // T5 saturated buckets / scale
@@ -1386,7 +1386,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 }
 
 bool fwd_variant_built(int kind, bool bf, Variant v) {
-  if (kind == 2) return v.qb == 1 && v.nw == (bf ? 8 : 4);
+  if (kind == 2) return v.qb == 1 && v.nw == 4;
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
 
@@ -1398,9 +1398,7 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
 #define RA_DT(K, QBV, NWV)                                                        \
   RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
   RA_CASE(K, false, 32, QBV, NWV)
-  RA_DT(0, 1, 4) RA_DT(1, 1, 4)
-  RA_CASE(2, true, 64, 1, 8) RA_CASE(2, true, 32, 1, 8)
-  RA_CASE(2, false, 64, 1, 4) RA_CASE(2, false, 32, 1, 4)
+  RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
   RA_CASE(1, true, 64, 2, 4) RA_CASE(1, true, 32, 2, 4)
 #undef RA_DT
