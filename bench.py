@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 from transformer_attention_relative_amd.synthetic import WORKLOADS, Workload, make_inputs, params_of  # noqa: E402
 
 DEFAULT_WORKLOAD = "t5_encoder_padded"
-SECONDARY = ["t5_decoder_kvcache", "shaw_causal_k16", "deberta_k512"]
+SECONDARY = ["t5_decoder_kvcache", "t5_decode_evicted", "shaw_causal_k16", "deberta_k512"]
 METRIC = "rel-pos attention fwd TFLOP/s and % of MFMA bf16 peak (1 MI355X)"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0                             # MI355X published HBM3E bandwidth
@@ -57,7 +57,10 @@ def _kv_limits(wl: Workload, kv_valid_len):
 def counted_work(wl: Workload, kv_valid_len):
     """(counted FLOPs, algorithmic bytes) of one forward call."""
     lims = _kv_limits(wl, kv_valid_len)
-    pos = wl.q_pos_offset + np.arange(wl.Lq, dtype=np.int64)
+    # query positions counted from key row 0 (every term depends on the
+    # difference of the absolute positions only)
+    qoff = wl.q_pos_offset - wl.k_pos_offset
+    pos = qoff + np.arange(wl.Lq, dtype=np.int64)
     esz = 4 if wl.dtype == "fp32" else 2
     flops = 0.0
     kv_bytes = 0.0
@@ -80,14 +83,14 @@ def counted_work(wl: Workload, kv_valid_len):
             # per key column: the query rows that see key j
             j = np.arange(wl.Lk, dtype=np.int64)
             if wl.causal:
-                first = np.maximum(j - wl.q_pos_offset, 0)          # first row with pos >= j
+                first = np.maximum(j - qoff, 0)                     # first row with pos >= j
                 nrows = np.where(j < lim, np.maximum(wl.Lq - first, 0), 0)
             else:
                 first = np.zeros_like(j)
                 nrows = np.where(j < lim, wl.Lq, 0)
             hasc = nrows > 0
-            p_first = wl.q_pos_offset + first
-            p_last = wl.q_pos_offset + wl.Lq - 1
+            p_first = qoff + first
+            p_last = qoff + wl.Lq - 1
             a_ = np.clip(j - p_last, -k, k - 1)
             b_ = np.clip(j - p_first, -k, k - 1)
             per_head += 2.0 * wl.d * np.where(hasc, b_ - a_ + 1, 0).sum()

@@ -13,18 +13,19 @@
  *   out[b,h,i,:] = sum_j softmax_j(s_ij) * value_ij
  *
  * over the keys j that are visible to row i, where, with absolute query
- * position p_i = q_pos_offset + i and key position j,
+ * position p_i = q_pos_offset + i and absolute key position
+ * t_j = k_pos_offset + j,
  *
- *   T5      s_ij = scale * q_i.k_j + table[bucket(j - p_i), h]
+ *   T5      s_ij = scale * q_i.k_j + table[bucket(t_j - p_i), h]
  *           value_ij = v_j
  *           bucket(): [RPE] "T5: one scalar per head, looked up by bucket"
  *           and [T5B] (offset = key - query; bidirectional splits the
  *           buckets by direction; causal bucketing clamps forward offsets
  *           to distance 0).  The bias is added after scaling.
- *   SHAW    s_ij = scale * q_i.(k_j + a_K[r_ij]),  r_ij = clip(j - p_i, -k, k) + k
+ *   SHAW    s_ij = scale * q_i.(k_j + a_K[r_ij]),  r_ij = clip(t_j - p_i, -k, k) + k
  *           value_ij = v_j + a_V[r_ij]
  *           [RPE] "Shaw et al.: learned vectors on keys and values".
- *   DEBERTA s_ij = scale * (q_i.k_j + q_i.Kr[d(p_i, j), h] + k_j.Qr[d(j, p_i), h])
+ *   DEBERTA s_ij = scale * (q_i.k_j + q_i.Kr[d(p_i, t_j), h] + k_j.Qr[d(t_j, p_i), h])
  *           d(x, y) = clip(x - y, -k, k - 1) + k, value_ij = v_j
  *           [DRPE] "The Relative Position Formula" (clip-and-shift index,
  *           2k rows); [RPE] "DeBERTa: disentangled content and position"
@@ -34,8 +35,16 @@
  * [RPE] "Failure modes"): T5 and Shaw index by key - query; DeBERTa's
  * d(i, j) takes query - key.
  *
- * Visibility: key j is hidden when causal != 0 and j > p_i, and when
- * kv_valid_len != NULL and j >= kv_valid_len[b].  Masking is independent of
+ * Visibility: key j is hidden when causal != 0 and t_j > p_i, and when
+ * kv_valid_len != NULL and j >= kv_valid_len[b] (a key index, not a
+ * position).
+ *
+ * Key positions: every term depends on positions only through t_j - p_i,
+ * so a cache whose oldest keys were dropped is described by k_pos_offset
+ * alone, and nothing stored needs rewriting ([RPE] "Kernels and the KV
+ * cache": offset-only biases survive eviction).  Lq = 1 with
+ * q_pos_offset = the new token's position is one decode step ([T5B],
+ * cached decoding).  Masking is independent of
  * bucketing ([T5B]): a forward offset that maps to bucket 0 is still hidden
  * under the causal mask.  A row with no visible key produces zeros.
  *
@@ -63,7 +72,8 @@
 extern "C" {
 #endif
 
-#define RELATTN_ABI_VERSION 1
+/* 2: relattn_params gained k_pos_offset */
+#define RELATTN_ABI_VERSION 2
 
 typedef enum {
     RELATTN_T5 = 0,
@@ -103,8 +113,9 @@ typedef struct {
     int32_t max_distance;    /* T5: distance where log buckets end (> exact range) */
     int32_t bidirectional;   /* T5: nonzero = split buckets by direction         */
     int32_t clip_k;          /* SHAW (1..32) / DEBERTA (1..65536): clip k        */
-    int32_t q_pos_offset;    /* absolute position of query row 0 (>= 0); keys
-                                sit at positions 0..Lk-1 ([T5B], cached decoder) */
+    int32_t q_pos_offset;    /* absolute position of query row 0 (>= 0)
+                                ([T5B], cached decoder)                         */
+    int32_t k_pos_offset;    /* absolute position of key row 0 (>= 0)          */
     int32_t causal;          /* nonzero: hide keys after the query's position    */
     const int32_t *kv_valid_len; /* device int32 [B] or NULL: keys j >= len hidden */
     float scale;             /* 0 = default: 1/sqrt(d) (T5, SHAW), 1/sqrt(3d)

@@ -35,7 +35,7 @@ def test_header_declares_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.relattn_abi_version() == 1
+    assert lib.relattn_abi_version() == 2
 
 
 def _params(**kw):
@@ -75,6 +75,8 @@ def _fwd_status(lib, p):
     (dict(kind="t5", table=FAKE, num_buckets=512), 1),
     (dict(kind="t5", table=FAKE, num_buckets=32, max_distance=100000), 2),  # LUT too large
     (dict(kind="t5", table=FAKE, q_pos_offset=-1), 1),
+    (dict(kind="t5", table=FAKE, k_pos_offset=-1), 1),
+    (dict(kind="t5", table=FAKE, k_pos_offset=(1 << 28) - 10), 2),   # key positions too large
     (dict(kind="t5", table=FAKE, scale=-1.0), 1),
     (dict(kind="t5", table=FAKE, scale=float("inf")), 1),
     (dict(kind="shaw", table=FAKE, clip_k=4), 1),           # table2 NULL

@@ -62,13 +62,14 @@ def check_close(got, want, dtype, what=""):
 def test_rel_index_bit_exact_full_grid(name):
     wl = WORKLOADS[name]
     qpos = wl.q_pos_offset + np.arange(wl.Lq)
-    kpos = np.arange(wl.Lk)
+    kpos = wl.k_pos_offset + np.arange(wl.Lk)
     QP, KP = np.meshgrid(qpos, kpos, indexing="ij")
     qp = torch.from_numpy(QP.reshape(-1).astype(np.int32)).to(DEV)
     kp = torch.from_numpy(KP.reshape(-1).astype(np.int32)).to(DEV)
     kw = dict(num_buckets=wl.num_buckets, max_distance=wl.max_distance,
               bidirectional=wl.bidirectional, clip_k=wl.clip_k)
-    want = oracle.rel_index_matrices(wl.kind, wl.Lq, wl.Lk, q_pos_offset=wl.q_pos_offset, **kw)
+    want = oracle.rel_index_matrices(wl.kind, wl.Lq, wl.Lk, q_pos_offset=wl.q_pos_offset,
+                                     k_pos_offset=wl.k_pos_offset, **kw)
     got = ra.relattn_rel_index(wl.kind, qp, kp, 0, **kw).cpu().numpy().reshape(wl.Lq, wl.Lk)
     assert np.array_equal(got, want["idx"])
     if wl.kind == "deberta":
@@ -139,6 +140,7 @@ def _case_id(wl):
         s += f"-k{wl.clip_k}"
     s += "-causal" if wl.causal else ""
     s += f"-q{wl.q_pos_offset}" if wl.q_pos_offset else ""
+    s += f"-k{wl.k_pos_offset}" if wl.k_pos_offset else ""
     s += "-pad" if wl.valid_len_range else ""
     return s
 
@@ -179,6 +181,93 @@ def test_parity_split_kv(wl):
     got = run_gpu(wl, _to_dev(inp)).cpu()
     want = run_oracle(wl, inp)
     check_close(got.float().numpy(), want, wl.dtype, _case_id(wl))
+
+
+# ----------------------------------------------------------------------------
+# 2b. key positions (a cache whose oldest keys were dropped: [RPE] "Kernels
+#     and the KV cache") and one-token decode steps ([T5B], cached decoding)
+# ----------------------------------------------------------------------------
+
+def _kp(kind, dtype, d, **kw):
+    base = dict(name="kpos", kind=kind, B=2, H=3, Lq=130, Lk=400, d=d, dtype=dtype,
+                table_sigma=0.5 if kind == "t5" else 0.1)
+    base.update(kw)
+    return Workload(**base)
+
+
+KPOS_CASES = []
+for dtype, d in (("bf16", 64), ("fp32", 32)):
+    KPOS_CASES += [
+        # keys 1700..2099, queries 2000..2129
+        _kp("t5", dtype, d, bidirectional=False, causal=True, q_pos_offset=2000, k_pos_offset=1700),
+        # every key after every query (forward offsets only)
+        _kp("t5", dtype, d, Lq=200, Lk=250, q_pos_offset=0, k_pos_offset=300),
+        _kp("t5", dtype, d, num_buckets=64, max_distance=100, q_pos_offset=64, k_pos_offset=20,
+            valid_len_range=(100, 400)),
+        _kp("shaw", dtype, d, clip_k=16, causal=True, Lq=100, Lk=200, q_pos_offset=500,
+            k_pos_offset=450),
+        _kp("shaw", dtype, d, clip_k=5, Lq=90, Lk=150, q_pos_offset=10, k_pos_offset=1000),
+        _kp("deberta", dtype, d, clip_k=40, q_pos_offset=100, k_pos_offset=180),
+        _kp("deberta", dtype, d, clip_k=512, causal=True, Lq=90, Lk=500, q_pos_offset=1000,
+            k_pos_offset=700),
+        # the first 50 query rows see no key at all (their keys lie ahead)
+        _kp("shaw", dtype, d, clip_k=8, causal=True, Lq=120, Lk=200, q_pos_offset=300,
+            k_pos_offset=350),
+    ]
+
+
+@pytest.mark.parametrize("wl", KPOS_CASES, ids=_case_id)
+def test_parity_key_positions(wl):
+    inp = make_inputs(wl, seed=13)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    check_close(got, want, wl.dtype, _case_id(wl))
+    if wl.causal:
+        # rows whose position precedes every key are exactly zero
+        dead = wl.q_pos_offset + np.arange(wl.Lq) < wl.k_pos_offset
+        assert not np.any(got[:, :, dead])
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+def test_keys_all_ahead_of_queries_give_zeros(kind):
+    wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else 8, bidirectional=False,
+             causal=True, Lq=64, Lk=100, q_pos_offset=10, k_pos_offset=74)
+    got = run_gpu(wl, _to_dev(make_inputs(wl, seed=14))).cpu()
+    assert torch.count_nonzero(got) == 0
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+def test_shifting_both_positions_changes_nothing(kind):
+    # every term depends on key position - query position only ([RPE]:
+    # shifting the input by a constant must leave the output unchanged), so
+    # the kernels see identical inputs and the outputs are bit-identical
+    wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else 12, bidirectional=False,
+             causal=True, Lq=150, Lk=300, q_pos_offset=200, k_pos_offset=60)
+    dev = _to_dev(make_inputs(wl, seed=15))
+    a = run_gpu(wl, dev).clone()
+    b = run_gpu(wl.replace(q_pos_offset=200 + 777, k_pos_offset=60 + 777), dev)
+    assert torch.equal(a, b)
+
+
+DECODE1_CASES = [
+    Workload(name="dec1", kind="t5", B=2, H=4, Lq=1, Lk=4096, d=64, dtype="bf16",
+             bidirectional=False, causal=True, q_pos_offset=4095),
+    WORKLOADS["t5_decode_evicted"].replace(B=2, H=3),
+    Workload(name="dec1", kind="t5", B=1, H=3, Lq=1, Lk=1500, d=32, dtype="fp32",
+             bidirectional=False, causal=True, q_pos_offset=1999, k_pos_offset=500),
+    Workload(name="dec1", kind="shaw", B=2, H=2, Lq=1, Lk=2000, d=64, dtype="bf16",
+             clip_k=16, causal=True, q_pos_offset=2999, k_pos_offset=1000, table_sigma=0.1),
+    Workload(name="dec1", kind="deberta", B=1, H=4, Lq=1, Lk=1500, d=64, dtype="bf16",
+             clip_k=512, causal=True, q_pos_offset=1600, k_pos_offset=100, table_sigma=0.1),
+]
+
+
+@pytest.mark.parametrize("wl", DECODE1_CASES, ids=_case_id)
+def test_parity_decode_one_token(wl):
+    inp = make_inputs(wl, seed=16)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    check_close(got, want, wl.dtype, _case_id(wl))
 
 
 # ----------------------------------------------------------------------------

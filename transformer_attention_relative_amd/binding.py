@@ -36,7 +36,8 @@ class relattn_params(ctypes.Structure):
         ("table", ctypes.c_void_p), ("table2", ctypes.c_void_p),
         ("num_buckets", ctypes.c_int32), ("max_distance", ctypes.c_int32),
         ("bidirectional", ctypes.c_int32), ("clip_k", ctypes.c_int32),
-        ("q_pos_offset", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("q_pos_offset", ctypes.c_int32), ("k_pos_offset", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
         ("kv_valid_len", ctypes.c_void_p), ("scale", ctypes.c_float),
     ]
 
@@ -94,11 +95,12 @@ def _ptr(t) -> Optional[int]:
 def make_params(kind: str, dtype: str, B: int, H: int, Lq: int, Lk: int, d: int, *,
                 table=None, table2=None, num_buckets: int = 32, max_distance: int = 128,
                 bidirectional: bool = True, clip_k: int = 0, q_pos_offset: int = 0,
-                causal: bool = False, kv_valid_len=None, scale: float = 0.0) -> relattn_params:
+                k_pos_offset: int = 0, causal: bool = False, kv_valid_len=None,
+                scale: float = 0.0) -> relattn_params:
     return relattn_params(
         KINDS[kind], DTYPES[dtype], B, H, Lq, Lk, d, _ptr(table), _ptr(table2),
         num_buckets, max_distance, int(bool(bidirectional)), clip_k, q_pos_offset,
-        int(bool(causal)), _ptr(kv_valid_len), float(scale))
+        k_pos_offset, int(bool(causal)), _ptr(kv_valid_len), float(scale))
 
 
 def _stream_handle(device) -> int:
@@ -115,13 +117,15 @@ def relattn_workspace_bytes(params: relattn_params) -> int:
 
 def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int = 32,
                 max_distance: int = 128, bidirectional: bool = True, clip_k: int = 0,
-                q_pos_offset: int = 0, causal: bool = False, kv_valid_len=None,
-                scale: float = 0.0, out=None, workspace=None):
+                q_pos_offset: int = 0, k_pos_offset: int = 0, causal: bool = False,
+                kv_valid_len=None, scale: float = 0.0, out=None, workspace=None):
     """Fused forward on the current HIP stream; returns ``out``.
 
     q [B, H, Lq, d], k/v [B, H, Lk, d] (float32 or bfloat16, contiguous, on
     the GPU).  Tables: T5 float32 [num_buckets, H]; Shaw a_K / a_V
-    [2k+1, d]; DeBERTa Kr / Qr [2k, H, d] (input dtype).  ``kv_valid_len``:
+    [2k+1, d]; DeBERTa Kr / Qr [2k, H, d] (input dtype).  Query row i sits at
+    absolute position ``q_pos_offset + i``, key row j at ``k_pos_offset + j``.
+    ``kv_valid_len``:
     int32 [B] on the GPU or None.  ``out`` and ``workspace`` are allocated
     with torch when not given.
     """
@@ -148,7 +152,8 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
     p = make_params(kind, dtype, B, H, Lq, Lk, d, table=table, table2=table2,
                     num_buckets=num_buckets, max_distance=max_distance,
                     bidirectional=bidirectional, clip_k=clip_k, q_pos_offset=q_pos_offset,
-                    causal=causal, kv_valid_len=kv_valid_len, scale=scale)
+                    k_pos_offset=k_pos_offset, causal=causal, kv_valid_len=kv_valid_len,
+                    scale=scale)
     if out is None:
         out = torch.empty_like(q)
     nbytes = relattn_workspace_bytes(p)

@@ -125,6 +125,9 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   if (p->q_pos_offset < 0) return fail(RELATTN_ERR_INVALID, "q_pos_offset=%d < 0", p->q_pos_offset);
   if ((int64_t)p->q_pos_offset + p->Lq > (1 << 28))
     return fail(RELATTN_ERR_UNSUPPORTED, "query positions above 2^28");
+  if (p->k_pos_offset < 0) return fail(RELATTN_ERR_INVALID, "k_pos_offset=%d < 0", p->k_pos_offset);
+  if ((int64_t)p->k_pos_offset + p->Lk > (1 << 28))
+    return fail(RELATTN_ERR_UNSUPPORTED, "key positions above 2^28");
   if (!(p->scale >= 0.f) || std::isinf(p->scale))
     return fail(RELATTN_ERR_INVALID, "scale must be finite and >= 0 (0 = default)");
   if (!p->table) return fail(RELATTN_ERR_INVALID, "table is NULL");
@@ -184,7 +187,11 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   const int BQ = kBlockRows * var.qb * var.nw;
   P->n_qtiles = (p->Lq + BQ - 1) / BQ;
   const int64_t wgs = (int64_t)BH * P->n_qtiles;
-  const int64_t kv_reach = p->causal ? std::min<int64_t>(p->Lk, (int64_t)p->q_pos_offset + p->Lq) : p->Lk;
+  // keys visible to the last query row (causal): key index j sees rows with
+  // q_pos_offset + i >= k_pos_offset + j
+  const int64_t qoff = (int64_t)p->q_pos_offset - p->k_pos_offset;
+  const int64_t kv_reach =
+      p->causal ? std::max<int64_t>(0, std::min<int64_t>(p->Lk, qoff + p->Lq)) : p->Lk;
   const int64_t kt = (kv_reach + kBK - 1) / kBK;
   int splits = 1;
   // Split the key range only when there are fewer workgroups than CUs
@@ -278,7 +285,8 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
   a.table = p->table; a.table2 = p->table2;
   a.kv_valid_len = p->kv_valid_len;
   a.B = p->B; a.H = p->H; a.Lq = p->Lq; a.Lk = p->Lk;
-  a.q_pos_offset = p->q_pos_offset;
+  // the kernels see positions relative to key row 0 (may be negative)
+  a.q_pos_offset = p->q_pos_offset - p->k_pos_offset;
   a.causal = p->causal ? 1 : 0;
   a.clip_k = p->clip_k;
   a.scale = P.scale;

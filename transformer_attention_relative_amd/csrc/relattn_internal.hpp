@@ -36,7 +36,8 @@ struct FwdArgs {
   float *part_ml;  // split-KV row stats        [n_splits][B*H][Lq][2] (log2 max, sum)
   const void *colc; // DeBERTa per-key constants [B*H][Lk] x 8 bytes (relattn_colc_kernel)
   int32_t B, H, Lq, Lk;
-  int32_t q_pos_offset, causal;
+  int32_t q_pos_offset;  // query row 0 minus key row 0 (absolute positions; may be < 0)
+  int32_t causal;
   int32_t clip_k;
   float scale;      // multiplies the raw score
   float scale_log2; // scale * log2(e)

@@ -37,6 +37,7 @@ class Workload:
     bidirectional: bool = True
     clip_k: int = 0
     q_pos_offset: int = 0
+    k_pos_offset: int = 0
     causal: bool = False
     valid_len_range: Optional[tuple] = None   # (lo, hi) inclusive, per sequence
     table_sigma: float = 0.5
@@ -77,6 +78,13 @@ WORKLOADS = {
         q_pos_offset=3968, causal=True, table_sigma=0.5,
         description="T5 causal decoder with KV cache: 128 queries at positions "
                     "3968..4095 against keys 0..4095, B4 H16 d64 bf16"),
+    "t5_decode_evicted": Workload(
+        name="t5_decode_evicted", kind="t5", B=4, H=16, Lq=1, Lk=3072, d=64,
+        dtype="bf16", num_buckets=32, max_distance=128, bidirectional=False,
+        q_pos_offset=4095, k_pos_offset=1024, causal=True, table_sigma=0.5,
+        description="T5 causal decode step: one query at position 4095 against "
+                    "a cache whose first 1024 keys were evicted (keys at "
+                    "positions 1024..4095), B4 H16 d64 bf16"),
     "shaw_causal_k16": Workload(
         name="shaw_causal_k16", kind="shaw", B=4, H=16, Lq=4096, Lk=4096, d=64,
         dtype="bf16", clip_k=16, causal=True, table_sigma=0.1,
@@ -120,4 +128,5 @@ def params_of(wl: Workload) -> dict:
     """Keyword arguments shared by the library binding and the oracle."""
     return dict(num_buckets=wl.num_buckets, max_distance=wl.max_distance,
                 bidirectional=wl.bidirectional, clip_k=wl.clip_k,
-                q_pos_offset=wl.q_pos_offset, causal=wl.causal)
+                q_pos_offset=wl.q_pos_offset, k_pos_offset=wl.k_pos_offset,
+                causal=wl.causal)
