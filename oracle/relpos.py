@@ -21,6 +21,10 @@ notes of the repository):
   * Shaw: "scaled as usual" = the whole q.(k + a_K) is multiplied by scale.
   * DeBERTa: c2p = q_i . Kr[delta(i,j)], p2c = k_j . Qr[delta(j,i)], the sum
     of the three terms times 1/sqrt(3d), d = head dimension.
+  * ALiBi ([RPE] "ALiBi and RoPE: the two endpoints": T5 with the table
+    removed, a fixed slope per head times the distance): bias = slope[h] *
+    |key position - query position|, added after scaling like T5's bias;
+    the slope carries its sign (negative slopes penalise distance).
   * Keys sit at absolute positions k_pos_offset + j; queries at
     q_pos_offset + i.  Padding masks key *index* j >= n_valid.
   * A row with no visible key has output 0.
@@ -37,7 +41,7 @@ import math
 
 import numpy as np
 
-KINDS = ("t5", "shaw", "deberta")
+KINDS = ("t5", "shaw", "deberta", "alibi")
 
 
 # --------------------------------------------------------------------------
@@ -149,8 +153,9 @@ def rel_index_matrices(kind: str, Lq: int, Lk: int, *, q_pos_offset: int = 0,
                        clip_k: int = 0, rows=None):
     """Integer index matrices [n_rows, Lk] for one kind.
 
-    Returns ``idx`` (T5 bucket / Shaw row / DeBERTa delta(i, j)) and, for
-    DeBERTa, ``idx2`` = delta(j, i) used by the position-to-content term.
+    Returns ``idx`` (T5 bucket / Shaw row / DeBERTa delta(i, j) / ALiBi
+    distance |key - query|) and, for DeBERTa, ``idx2`` = delta(j, i) used by
+    the position-to-content term.
     Offsets use absolute positions q_pos_offset + i and k_pos_offset + j;
     [T5B] (cached decoder paragraph) requires absolute query positions.
     """
@@ -166,6 +171,8 @@ def rel_index_matrices(kind: str, Lq: int, Lk: int, *, q_pos_offset: int = 0,
     if kind == "deberta":
         return {"idx": deberta_delta(-key_minus_query, clip_k),
                 "idx2": deberta_delta(key_minus_query, clip_k)}
+    if kind == "alibi":
+        return {"idx": np.abs(key_minus_query)}
     raise ValueError(f"unknown kind {kind!r}")
 
 
@@ -196,7 +203,8 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
                  form": Q times the 2k+1 vectors, gathered by clipped offset)
          DeBERTa R[i, j] = (Q Kr_h^T)[i, delta(i,j)] + (K Qr_h^T)[j, delta(j,i)]
                                                 ([RPE] DeBERTa; [DRPE])
-      4. logits: T5 q.k*scale + bias; Shaw/DeBERTa (q.k + R)*scale;
+         ALiBi   bias[i, j] = slope[h] * distance    ([RPE] ALiBi and RoPE)
+      4. logits: T5 / ALiBi q.k*scale + bias; Shaw/DeBERTa (q.k + R)*scale;
       5. masks: causal hides keys after the query's position; padding hides
          key index j >= n_valid ([T5B]: masking is separate from bucketing);
       6. softmax over visible keys;
@@ -225,6 +233,9 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
         tab = np.asarray(table, dtype=np.float64)
         bias = tab[idx["idx"], h]
         logits = content * scale + bias
+    elif kind == "alibi":
+        slope = float(np.asarray(table, dtype=np.float64).reshape(-1)[h])
+        logits = content * scale + slope * idx["idx"]
     elif kind == "shaw":
         a_k = np.asarray(table, dtype=np.float64)
         rel_keys = qr @ a_k.T                       # [n, 2k+1]
@@ -272,7 +283,7 @@ def relattn_forward(q, k, v, kind: str, table=None, table2=None, *,
     ``heads`` (list of (b, h)) and ``rows`` restrict the work for sampled
     comparisons; the result then has shape [len(heads), len(rows), d].
     Otherwise the result is [B, H, Lq, d].  Tables: T5 [num_buckets, H];
-    Shaw a_K, a_V [2k+1, d]; DeBERTa Kr, Qr [2k, H, d].
+    Shaw a_K, a_V [2k+1, d]; DeBERTa Kr, Qr [2k, H, d]; ALiBi slopes [H].
     """
     q = np.asarray(q)
     B, H, Lq, d = q.shape
@@ -363,6 +374,8 @@ def relattn_forward_bruteforce(q, k, v, kind: str, h: int, table=None, table2=No
             if kind == "t5":
                 b = t5_bucket(pj - pi, bidirectional, num_buckets, max_distance)
                 s = dot(q[i], k[j]) * scale + float(np.asarray(table)[b, h])
+            elif kind == "alibi":
+                s = dot(q[i], k[j]) * scale + float(np.asarray(table).reshape(-1)[h]) * abs(pj - pi)
             elif kind == "shaw":
                 s = dot(q[i], [a + b for a, b in zip(k[j], pair_key[i][j])]) * scale
             else:

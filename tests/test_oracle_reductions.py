@@ -61,6 +61,8 @@ def test_zero_tables_reduce_to_plain_attention(causal, n_valid, q_off):
     z = np.zeros((10, 1, d))
     got = oracle.relattn_forward_head(q, k, v, "deberta", 0, z, z, clip_k=5, **common)
     np.testing.assert_allclose(got, want_deb, atol=ATOL)
+    got = oracle.relattn_forward_head(q, k, v, "alibi", 0, np.zeros(1), **common)
+    np.testing.assert_allclose(got, want, atol=ATOL)
 
 
 @pytest.mark.parametrize("bidir", [True, False])
@@ -185,6 +187,7 @@ def test_position_shift_leaves_output_unchanged():
     rng = np.random.default_rng(9)
     q, k, v = _rand(rng, 10, 8), _rand(rng, 14, 8), _rand(rng, 14, 8)
     cases = {"t5": (_rand(rng, 32, 1), None, {}),
+             "alibi": (_rand(rng, 1), None, {}),
              "shaw": (_rand(rng, 9, 8), _rand(rng, 9, 8), dict(clip_k=4)),
              "deberta": (_rand(rng, 10, 1, 8), _rand(rng, 10, 1, 8), dict(clip_k=5))}
     for kind, (t1, t2, kw) in cases.items():
@@ -208,7 +211,7 @@ def test_rows_selection_matches_full():
 # -------------------------------------------------------------- brute force
 
 @settings(max_examples=60, deadline=None)
-@given(kind=st.sampled_from(["t5", "shaw", "deberta"]),
+@given(kind=st.sampled_from(["t5", "shaw", "deberta", "alibi"]),
        Lq=st.integers(1, 9), Lk=st.integers(1, 12), d=st.sampled_from([2, 4, 8]),
        q_off=st.integers(0, 40), k_off=st.integers(0, 40), causal=st.booleans(),
        bidir=st.booleans(), nb=st.sampled_from([4, 8, 16, 32, 64]),
@@ -224,6 +227,8 @@ def test_vectorised_equals_bruteforce(kind, Lq, Lk, d, q_off, k_off, causal, bid
     q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
     if kind == "t5":
         t1, t2 = _rand(rng, nb, H), None
+    elif kind == "alibi":
+        t1, t2 = _rand(rng, H, s=0.3), None
     elif kind == "shaw":
         t1, t2 = _rand(rng, 2 * clip + 1, d), _rand(rng, 2 * clip + 1, d)
     else:
@@ -233,3 +238,56 @@ def test_vectorised_equals_bruteforce(kind, Lq, Lk, d, q_off, k_off, causal, bid
     a = oracle.relattn_forward_head(q, k, v, kind, h, t1, t2, **kw)
     b = oracle.relattn_forward_bruteforce(q, k, v, kind, h, t1, t2, **kw)
     np.testing.assert_allclose(a, b, atol=1e-11, rtol=0)
+
+
+# -------------------------------------------------------------------- ALiBi
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alibi_is_t5_with_a_linear_table(causal):
+    # [RPE] "ALiBi and RoPE": ALiBi is T5 with the table removed, a slope per
+    # head times the distance.  Inside T5's exact range (distance < 8 at
+    # bidirectional 32/128, < 16 causal) a T5 table whose exact slots hold
+    # slope * distance gives the same logits, so the outputs agree.
+    rng = np.random.default_rng(21)
+    H, d = 3, 8
+    L = 8                                        # every |offset| <= 7
+    q, k, v = _rand(rng, L, d), _rand(rng, L, d), _rand(rng, L, d)
+    slopes = np.array([-0.5, 0.25, -0.0625])
+    table = np.zeros((32, H))
+    bidir = not causal
+    for dist in range(8):
+        if bidir:
+            table[dist] = slopes * dist           # keys at or before the query
+            table[16 + dist] = slopes * dist      # keys after it
+        else:
+            table[dist] = slopes * dist           # causal: bucket = distance
+    for h in range(H):
+        a = oracle.relattn_forward_head(q, k, v, "alibi", h, slopes, causal=causal,
+                                        q_pos_offset=4, k_pos_offset=4)
+        b = oracle.relattn_forward_head(q, k, v, "t5", h, table, bidirectional=bidir,
+                                        causal=causal, q_pos_offset=4, k_pos_offset=4)
+        np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def test_alibi_dense_bias_matches_sdpa():
+    # the bias materialised as an L x L float mask, through torch's attention
+    rng = np.random.default_rng(22)
+    Lq, Lk, d = 11, 19, 8
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    slope = -0.37
+    qpos = 30 + np.arange(Lq)[:, None]
+    kpos = 25 + np.arange(Lk)[None, :]
+    mask = slope * np.abs(kpos - qpos)
+    want = _sdpa(q, k, v, mask, 1 / math.sqrt(d))
+    got = oracle.relattn_forward_head(q, k, v, "alibi", 0, np.array([slope]),
+                                      q_pos_offset=30, k_pos_offset=25)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+def test_alibi_steep_penalty_reads_the_key_at_distance_zero():
+    # a large negative slope leaves only the key at the query's own position
+    rng = np.random.default_rng(23)
+    L, d = 12, 8
+    q, k, v = _rand(rng, L, d), _rand(rng, L, d), _rand(rng, L, d)
+    got = oracle.relattn_forward_head(q, k, v, "alibi", 0, np.array([-200.0]))
+    np.testing.assert_allclose(got, v, atol=1e-12)
