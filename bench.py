@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 from transformer_attention_relative_amd.synthetic import WORKLOADS, Workload, make_inputs, params_of  # noqa: E402
 
 DEFAULT_WORKLOAD = "t5_encoder_padded"
-SECONDARY = ["t5_decoder_kvcache", "t5_decode_evicted", "shaw_causal_k16", "deberta_k512"]
+SECONDARY = ["t5_decoder_kvcache", "t5_decode_evicted", "shaw_causal_k16", "deberta_k512",
+             "alibi_causal"]
 METRIC = "rel-pos attention fwd TFLOP/s and % of MFMA bf16 peak (1 MI355X)"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0                             # MI355X published HBM3E bandwidth
@@ -102,6 +103,8 @@ def counted_work(wl: Workload, kv_valid_len):
         tab = wl.num_buckets * wl.H * 4
     elif wl.kind == "shaw":
         tab = 2 * (2 * k + 1) * wl.d * esz
+    elif wl.kind == "alibi":
+        tab = wl.H * 4
     else:
         tab = 2 * (2 * k) * wl.H * wl.d * esz
     return flops, qo_bytes + kv_bytes + tab

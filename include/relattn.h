@@ -30,6 +30,11 @@
  *           [DRPE] "The Relative Position Formula" (clip-and-shift index,
  *           2k rows); [RPE] "DeBERTa: disentangled content and position"
  *           (content-to-position plus position-to-content, scale 1/sqrt(3d)).
+ *   ALIBI   s_ij = scale * q_i.k_j + slope[h] * |t_j - p_i|,  value_ij = v_j
+ *           [RPE] "ALiBi and RoPE: the two endpoints" (T5 with the table
+ *           removed: a fixed slope per head times the distance, no maximum
+ *           distance).  The slope carries its sign: a negative slope
+ *           penalises distance.
  *
  * Offset conventions (documented because mixing them swaps past and future,
  * [RPE] "Failure modes"): T5 and Shaw index by key - query; DeBERTa's
@@ -72,13 +77,14 @@
 extern "C" {
 #endif
 
-/* 2: relattn_params gained k_pos_offset */
+/* 2: relattn_params gained k_pos_offset; kind RELATTN_ALIBI */
 #define RELATTN_ABI_VERSION 2
 
 typedef enum {
     RELATTN_T5 = 0,
     RELATTN_SHAW = 1,
-    RELATTN_DEBERTA = 2
+    RELATTN_DEBERTA = 2,
+    RELATTN_ALIBI = 3
 } relattn_kind;
 
 typedef enum {
@@ -101,7 +107,8 @@ typedef enum {
  *   SHAW    table  : a_K [2*clip_k + 1, d] (dtype)  table2 : a_V, same shape;
  *           shared by all heads ([RPE] Shaw section)
  *   DEBERTA table  : Kr [2*clip_k, H, d] (dtype)    table2 : Qr, same shape
- * Device pointers must be 16-byte aligned.
+ *   ALIBI   table  : float32 slopes [H]             table2 : unused (NULL)
+ * Device pointers must be 16-byte aligned (ALiBi slopes: 4-byte).
  */
 typedef struct {
     int32_t kind;            /* relattn_kind                                     */
@@ -143,7 +150,7 @@ relattn_status relattn_workspace_bytes(const relattn_params *p, size_t *bytes);
  * Relative index of n (query position, key position) pairs, computed by the
  * same device index functions the fused kernel uses:
  *   which = 0: T5 bucket(k_pos - q_pos) | SHAW clip(k_pos - q_pos, -k, k) + k |
- *              DEBERTA d(q_pos, k_pos)
+ *              DEBERTA d(q_pos, k_pos) | ALIBI |k_pos - q_pos|
  *   which = 1: DEBERTA d(k_pos, q_pos) (position-to-content index); other
  *              kinds reject it.
  * Only kind and the kind's index parameters of *p are read (shapes and

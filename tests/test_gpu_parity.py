@@ -96,6 +96,7 @@ def test_index_page_values_on_gpu():
     k = torch.tensor([0, 17, 0, 17, 124], dtype=torch.int32, device=DEV)
     assert ra.relattn_rel_index("t5", q[:2], k[:2], bidirectional=True).tolist() == [10, 26]
     assert ra.relattn_rel_index("t5", q, k, bidirectional=False).tolist() == [16, 0, 16, 0, 4]
+    assert ra.relattn_rel_index("alibi", q, k).tolist() == [17, 17, 17, 17, 4]
     kk = 512
     q = torch.tensor([0, 5, 520], dtype=torch.int32, device=DEV)
     k = torch.tensor([kk, 5, 9], dtype=torch.int32, device=DEV)   # i - j = -k, 0, k - 1
@@ -129,6 +130,9 @@ for dtype in ("fp32", "bf16"):
             _small("deberta", dtype, d, clip_k=16, valid_len_range=(50, 333)),
             _small("deberta", dtype, d, clip_k=3, causal=True, Lq=333),
             _small("deberta", dtype, d, clip_k=40, causal=True, Lq=100, q_pos_offset=233),
+            _small("alibi", dtype, d),
+            _small("alibi", dtype, d, causal=True, Lq=333),
+            _small("alibi", dtype, d, causal=True, Lq=200, q_pos_offset=133, valid_len_range=(1, 333)),
         ]
 
 
@@ -213,6 +217,8 @@ for dtype, d in (("bf16", 64), ("fp32", 32)):
         # the first 50 query rows see no key at all (their keys lie ahead)
         _kp("shaw", dtype, d, clip_k=8, causal=True, Lq=120, Lk=200, q_pos_offset=300,
             k_pos_offset=350),
+        _kp("alibi", dtype, d, causal=True, q_pos_offset=2000, k_pos_offset=1700),
+        _kp("alibi", dtype, d, Lq=200, Lk=250, q_pos_offset=0, k_pos_offset=300),
     ]
 
 
@@ -228,7 +234,7 @@ def test_parity_key_positions(wl):
         assert not np.any(got[:, :, dead])
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
 def test_keys_all_ahead_of_queries_give_zeros(kind):
     wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else 8, bidirectional=False,
              causal=True, Lq=64, Lk=100, q_pos_offset=10, k_pos_offset=74)
@@ -236,7 +242,7 @@ def test_keys_all_ahead_of_queries_give_zeros(kind):
     assert torch.count_nonzero(got) == 0
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
 def test_shifting_both_positions_changes_nothing(kind):
     # every term depends on key position - query position only ([RPE]:
     # shifting the input by a constant must leave the output unchanged), so
@@ -259,7 +265,25 @@ DECODE1_CASES = [
              clip_k=16, causal=True, q_pos_offset=2999, k_pos_offset=1000, table_sigma=0.1),
     Workload(name="dec1", kind="deberta", B=1, H=4, Lq=1, Lk=1500, d=64, dtype="bf16",
              clip_k=512, causal=True, q_pos_offset=1600, k_pos_offset=100, table_sigma=0.1),
+    Workload(name="dec1", kind="alibi", B=2, H=8, Lq=1, Lk=3000, d=64, dtype="bf16",
+             causal=True, q_pos_offset=3999, k_pos_offset=1000),
 ]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_alibi_steep_slopes(causal, dtype):
+    # steep penalties (the nearest keys dominate, and the scores rise along
+    # the keys, so the row reference moves again and again) and a positive
+    # slope (the farthest keys dominate)
+    wl = _small("alibi", dtype, 64, H=4, Lq=300, Lk=333, causal=causal, q_pos_offset=33)
+    inp = make_inputs(wl, seed=17)
+    inp["table"] = torch.tensor([-2.0, -0.75, 0.05, -6.0], dtype=torch.float32)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    tol = STRESS_TOL[dtype] if dtype == "fp32" else TOL[dtype]
+    err = np.abs(got - want)
+    assert err.max() <= tol[0] and err.mean() <= tol[1], (err.max(), err.mean())
 
 
 @pytest.mark.parametrize("wl", DECODE1_CASES, ids=_case_id)
@@ -311,7 +335,7 @@ def test_deterministic(name):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
 def test_masked_keys_do_not_matter(kind):
     # [T5B]: check masking on its own -- perturbing keys that are hidden
     # (padding, or after the query under the causal mask) leaves the output

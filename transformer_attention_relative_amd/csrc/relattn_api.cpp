@@ -111,7 +111,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 relattn_status plan_problem(const relattn_params* p, Plan* P) {
   if (!p) return fail(RELATTN_ERR_INVALID, "params is NULL");
-  if (p->kind < 0 || p->kind > 2) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
+  if (p->kind < 0 || p->kind > 3) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
   if (p->dtype != RELATTN_FP32 && p->dtype != RELATTN_BF16)
     return fail(RELATTN_ERR_INVALID, "unknown dtype %d", p->dtype);
   if (p->B < 1 || p->H < 1 || p->Lq < 1 || p->Lk < 1)
@@ -131,7 +131,9 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   if (!(p->scale >= 0.f) || std::isinf(p->scale))
     return fail(RELATTN_ERR_INVALID, "scale must be finite and >= 0 (0 = default)");
   if (!p->table) return fail(RELATTN_ERR_INVALID, "table is NULL");
-  if (p->kind != RELATTN_T5) {
+  if (p->kind == RELATTN_ALIBI && (reinterpret_cast<uintptr_t>(p->table) & 3))
+    return fail(RELATTN_ERR_INVALID, "ALiBi slopes must be 4-byte aligned");
+  if (p->kind == RELATTN_SHAW || p->kind == RELATTN_DEBERTA) {
     if (!p->table2) return fail(RELATTN_ERR_INVALID, "table2 is NULL");
     if (!aligned16(p->table) || !aligned16(p->table2))
       return fail(RELATTN_ERR_INVALID, "tables must be 16-byte aligned");
@@ -324,7 +326,7 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
 relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, const int32_t* k_pos,
                                  int64_t n, int32_t which, int32_t* idx_out, void* stream) {
   if (!p) return fail(RELATTN_ERR_INVALID, "params is NULL");
-  if (p->kind < 0 || p->kind > 2) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
+  if (p->kind < 0 || p->kind > 3) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
   if (n < 0) return fail(RELATTN_ERR_INVALID, "n=%lld < 0", (long long)n);
   if (which != 0 && which != 1) return fail(RELATTN_ERR_INVALID, "which=%d not 0 or 1", which);
   if (which == 1 && p->kind != RELATTN_DEBERTA)
@@ -338,7 +340,7 @@ relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, 
     a.t5_slots = P.slots; a.t5_exact = P.exact; a.t5_bidir = p->bidirectional ? 1 : 0;
     a.t5_nthr = P.nthr;
     for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.nthr ? P.thr[m] : INT32_MAX;
-  } else {
+  } else if (p->kind != RELATTN_ALIBI) {
     if (p->clip_k < 1) return fail(RELATTN_ERR_INVALID, "clip_k=%d must be >= 1", p->clip_k);
   }
   if (n == 0) return ok();

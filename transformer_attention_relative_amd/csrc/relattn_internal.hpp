@@ -76,7 +76,9 @@ struct Variant {
 };
 
 // Key/value stages in flight (global -> LDS ring depth) per kind.
-RELATTN_HD constexpr int num_stages(int kind, bool bf16) { return kind == 0 ? (bf16 ? 4 : 3) : 2; }
+RELATTN_HD constexpr int num_stages(int kind, bool bf16) {
+  return (kind == 0 || kind == 3) ? (bf16 ? 4 : 3) : 2;
+}
 
 // Shaw bins strictly inside the clip window (offsets -k+1 .. k-1), padded to
 // whole MFMA contraction chunks.
@@ -137,10 +139,10 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     L.wscr_wave_bytes = rows * shaw_bin_stride(clip_k, esz) * esz;
     L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
     rel_bytes = L.avt_off + (bf16 ? d * nbin * 2 : 0);
-  } else {
+  } else if (kind == 2) {
     L.deb_wave_floats = kBlockRows * kCbandStride;
     rel_bytes = nw * L.deb_wave_floats * 4;
-  }
+  }  // ALIBI: nothing beyond the stages
   L.total = L.rel_off + ((rel_bytes + 15) & ~15);
   return L;
 }

@@ -123,6 +123,8 @@ __global__ void relattn_index_kernel(IndexArgs a) {
       r = t5_bucket_dev(kp - qp, a.t5_slots, a.t5_exact, a.t5_bidir, a.t5_nthr, a.t5_thr);
     } else if (a.kind == 1) {
       r = shaw_row_dev(kp - qp, a.clip_k);
+    } else if (a.kind == 3) {
+      r = abs(kp - qp);  // ALiBi distance
     } else {
       r = a.which == 0 ? deberta_delta_dev(qp - kp, a.clip_k) : deberta_delta_dev(kp - qp, a.clip_k);
     }
@@ -460,6 +462,14 @@ struct KeyConst<true> {
     const bf16 z = (bf16)0.f;
     v = hh == 0 ? bf16x8{x[0], x[1], x[2], x[3], z, z, z, z} : bf16x8{};
   }
+  // side-0 constant c0 and side-1 constant c1 of key lq, each as a bf16
+  // hi + lo pair
+  __device__ __forceinline__ void set(float c0, float c1, int hh) {
+    const bf16 h0 = (bf16)c0, h1 = (bf16)c1;
+    const bf16 l0 = (bf16)(c0 - (float)h0), l1 = (bf16)(c1 - (float)h1);
+    const bf16 z = (bf16)0.f;
+    v = hh == 0 ? bf16x8{h0, l0, h1, l1, z, z, z, z} : bf16x8{};
+  }
 };
 template <>
 struct KeyConst<false> {
@@ -467,6 +477,7 @@ struct KeyConst<false> {
   __device__ __forceinline__ void load(const void* colc, size_t base, int key, int hh) {
     v = reinterpret_cast<const float*>(colc)[(base + key) * 2 + hh];
   }
+  __device__ __forceinline__ void set(float c0, float c1, int hh) { v = hh == 0 ? c0 : c1; }
 };
 
 template <bool BF>
@@ -547,7 +558,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   // range under a valid length starts at a tile that depends on it, so its
   // first copies wait for it.
   const int causal_end = a.causal ? min(a.Lk, wg_pos_max + 1) : a.Lk;
-  const bool early_copies = a.n_splits == 1 || a.kv_valid_len == nullptr;
+  // Key tile of loop step r over the tile range [kb, ke).  ALiBi visits the
+  // tiles nearest the diagonal first: from the tile of the workgroup's
+  // middle query position down to kb, then upward from there; under a
+  // distance penalty a row's scores then mostly fall from tile to tile, so
+  // its reference rarely has to move.  The other kinds run upward.
+  const int wg_mid_tile = ((a.q_pos_offset + q0 + wg_pos_max) >> 1) >> 6;  // floor division
+  static_assert(kBK == 64, "wg_mid_tile divides by 64");
+  auto tile_at = [&](const int r, const int kb, const int ke) -> int {
+    if constexpr (KIND == 3) {
+      const int kc = min(max(wg_mid_tile, kb), ke - 1);
+      return r <= kc - kb ? kc - r : kb + r;
+    }
+    return kb + r;
+  };
+  // ALiBi's order needs the exact tile range, so its early copies wait for
+  // a per-sequence valid length
+  const bool early_copies =
+      KIND == 3 ? a.kv_valid_len == nullptr : (a.n_splits == 1 || a.kv_valid_len == nullptr);
   if (early_copies) {
     const int n_kt0 = (causal_end + kBK - 1) / kBK;
     const int per0 = (n_kt0 + a.n_splits - 1) / a.n_splits;
@@ -557,7 +585,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     dma.init(wave, lane);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-      if (s < n0) dma.issue(Kg, Vg, a.Lk, (beg0 + s) * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
+      if (s < n0)
+        dma.issue(Kg, Vg, a.Lk, tile_at(s, beg0, beg0 + n0) * kBK, smem + s * L.stage_bytes,
+                  L.tile_bytes, wave, lane);
   }
 
   // ---- register loads (valid length, Q fragments, the kind's small tables)
@@ -613,10 +643,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         }
       }
     }
-  } else {
+  } else if constexpr (KIND == 2) {
     const T* kr = reinterpret_cast<const T*>(a.table);
     const int u = (lq == 1) ? 2 * ck - 1 : 0;
     krow[0].load(kr + ((size_t)u * a.H + h) * D, hh);
+  }
+  // ALiBi: the head's slope in raw-score units per unit of distance, and the
+  // in-block key term of blocks whose keys all lie at or before every query
+  // (side 0: -slope * (key - the block's first key)) or at or after it
+  // (side 1: +slope * (key - first key)); the rest of the bias is a per-row
+  // constant of the block
+  float alibi_s = 0.f;
+  KeyConst<BF> alibi_kc;
+  if constexpr (KIND == 3) {
+    alibi_s = reinterpret_cast<const float*>(a.table)[h] / a.scale;
+    alibi_kc.set(-alibi_s * (float)lq, alibi_s * (float)lq, hh);
   }
 
   const int kv_lim = max(0, min(a.Lk, kv_valid));
@@ -715,7 +756,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         avt[e] = r < 2 * ck - 1 ? av[(size_t)(r + 1) * D + dd] : (T)0.f;
       }
     }
-  } else {
+  } else if constexpr (KIND == 2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const f32x16 acc = mma_frag0<BF, D>(krow[0], qf[qb]);
@@ -731,7 +772,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < n_my)
-        dma.issue(Kg, Vg, a.Lk, (kt_begin + s) * kBK, smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
+        dma.issue(Kg, Vg, a.Lk, tile_at(s, kt_begin, kt_end) * kBK, smem + s * L.stage_bytes,
+                  L.tile_bytes, wave, lane);
   }
 
   // ---- running state ------------------------------------------------------
@@ -796,15 +838,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 
   // Tile classes (wave-uniform):
   //   0: every block far from the diagonal band (the relative term is a
-  //      per-row constant, plus a Qr row folded into the query for DeBERTa),
-  //      no mask;
+  //      per-row constant, plus a per-key constant for DeBERTa; ALiBi: every
+  //      key on one side of every query, the bias linear in the key), no
+  //      mask;
   //   1: T5, every block inside the bucket table's range, no mask;
   //   2: anything else (band terms, masks, Shaw bins);
   //   3: nothing to do for this wave (past its causal reach).
   // Runs of equal class go through a loop of their own, so the lean loops
   // are not burdened with the registers of the general one.
   auto tile_class = [&](const int r) -> int {
-    const int k0 = (kt_begin + r) * kBK;
+    const int k0 = tile_at(r, kt_begin, kt_end) * kBK;
     if (!wave_active || (a.causal && k0 > pw_max_real)) return 3;
     bool far_all = true, near_all = true;
 #pragma unroll
@@ -814,7 +857,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       bool far;
       if constexpr (KIND == 0) far = omax <= -a.t5_lsat || omin >= a.t5_rsat;
       else if constexpr (KIND == 1) far = omin >= ck || omax <= -ck;
-      else far = -omax >= ck || -omin <= -ck;
+      else if constexpr (KIND == 2) far = -omax >= ck || -omin <= -ck;
+      else far = omax <= 0 || omin >= 0;  // ALiBi: every key on one side
       far_all = far_all && far;
       near_all = near_all && !far;
     }
@@ -834,7 +878,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     for (int qb = 0; qb < QB; ++qb) pos[qb] = pw_min + 32 * qb + lq;
     KOffsets<BF, D> ko;
     ko.init(lane);
-    const int kt = kt_begin + r;
+    const int kt = tile_at(r, kt_begin, kt_end);
     if constexpr (NS >= 3 && EVEN_LOADS) {
       // tiles newer than r that may still be in flight: min(NS - 2, n_my - 1 - r)
       const int newer = min(NS - 2, n_my - 1 - r);
@@ -850,8 +894,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       // copy offsets from a fresh lane id: kept out of registers between tiles
       Dma dma;
       dma.init(wave, opaque_lane());
-      dma.issue(Kg, Vg, a.Lk, (kt + NS - 1) * kBK, smem + ((r + NS - 1) % NS) * L.stage_bytes,
-                L.tile_bytes, wave, lane);
+      dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
+                smem + ((r + NS - 1) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
     }
     if constexpr (CLS == 3) return;
     const char* ktile = smem + (r % NS) * L.stage_bytes;
@@ -860,7 +904,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     // ---- the tile's query blocks (wave-uniform) ----
     float b_tile[QB];  // per-row constant of the tile's far blocks (raw score units)
     bool near[QB], far_right[QB];
-    int deb_side[QB];  // DeBERTa: 0 far-left tile, 1 far-right tile, -1 mixed
+    int deb_side[QB];  // DeBERTa / ALiBi: 0 far-left tile, 1 far-right tile, -1 mixed
     const float* lutp[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -886,9 +930,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         } else if (omax > -ck) {
           near[qb] = true;
         }
-      } else {
+      } else if constexpr (KIND == 2) {
         if (-omax >= ck) { deb_side[qb] = 0; b_tile[qb] = crow_hi[qb]; }       // every query - key >= k
         else if (-omin <= -ck) { deb_side[qb] = 1; b_tile[qb] = crow_lo[qb]; } // every query - key <= -k
+      } else {
+        if (omax <= 0) deb_side[qb] = 0;       // every key at or before every query
+        else if (omin >= 0) deb_side[qb] = 1;  // every key at or after every query
       }
     }
     // DeBERTa: the per-key constants of the tile's keys (for clipped blocks)
@@ -916,6 +963,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         const int tmin = pq_min - (j0 + 31), tmax = pq_max - j0;  // query - key over the block
         return tmin >= ck ? 0 : (tmax <= -ck ? 1 : -1);
       };
+      // ALiBi, per block: 0 / 1 every key on one side, -1 across the diagonal
+      auto alibi_side = [&](const int qb) -> int {
+        if (CLS == 0) return deb_side[qb];
+        const int pq_min = pw_min + 32 * qb;
+        return j0 + 31 <= pq_min ? 0 : (j0 >= pq_min + 31 ? 1 : -1);
+      };
       // per-row constant of this block (raw score units)
       auto b_block = [&](const int qb) -> float {
         if constexpr (KIND == 2) {
@@ -923,6 +976,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
             const int side = deb_block_side(qb);
             return side == 0 ? crow_hi[qb] : (side == 1 ? crow_lo[qb] : 0.f);
           }
+        }
+        if constexpr (KIND == 3) {
+          // slope * |key - query| = slope * (query - j0) - slope * (key - j0)
+          // left of the diagonal, the negation of both terms right of it
+          const int side = alibi_side(qb);
+          const float dist = (float)(pos[qb] - j0);
+          return side == 0 ? alibi_s * dist : (side == 1 ? -alibi_s * dist : 0.f);
         }
         return b_tile[qb];
       };
@@ -955,6 +1015,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
             s = mma_frag<BF, D>(kf, qf[qb], init);
           } else {
             s = mma_frag0<BF, D>(kf, qf[qb]);
+          }
+        } else if constexpr (KIND == 3) {
+          const int side = alibi_side(qb);
+          if (side >= 0) {
+            s = mma_keyconst<BF>(alibi_kc, side, hh);
+            s = mma_frag<BF, D>(kf, qf[qb], s);
+          } else {
+            // a block across the diagonal: the whole bias, per element
+            const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
+            f32x16 init;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) init[i] = alibi_s * (float)abs(obase + acc_row(i, 0));
+            s = mma_frag<BF, D>(kf, qf[qb], init);
           }
         } else {
           const int side = CLS == 0 ? deb_side[qb] : deb_block_side(qb);
@@ -1089,7 +1162,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (!((QM >> qb) & 1)) continue;
-        softmax(qb, c, (KIND == 2 && CLS == 2) ? ref_offset(c * b_block(qb), m_ref[qb]) : off[qb]);
+        softmax(qb, c, (KIND == 3 || (KIND == 2 && CLS == 2)) ? ref_offset(c * b_block(qb), m_ref[qb])
+                                                              : off[qb]);
         bad = bad || lsum[qb] > kSumLimit;
       }
       if (__builtin_expect(__any(bad), 0)) {
@@ -1386,7 +1460,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 }
 
 bool fwd_variant_built(int kind, bool bf, Variant v) {
-  if (kind == 2) return v.qb == 1 && v.nw == 4;
+  if (kind == 2) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
 
@@ -1398,9 +1472,10 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
 #define RA_DT(K, QBV, NWV)                                                        \
   RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
   RA_CASE(K, false, 32, QBV, NWV)
-  RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4)
+  RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
   RA_CASE(1, true, 64, 2, 4) RA_CASE(1, true, 32, 2, 4)
+  RA_CASE(3, true, 64, 2, 4) RA_CASE(3, true, 32, 2, 4)
 #undef RA_DT
 #undef RA_CASE
   return hipErrorInvalidValue;

@@ -10,8 +10,9 @@ draws are float32 ``randn`` times the stated standard deviation, in the
 order Q, K, V, table, table2, then the per-sequence valid key lengths
 (``randint(lo, hi + 1)``); Q/K/V (and the Shaw / DeBERTa tables) are then
 rounded to the workload dtype on the CPU (round to nearest even).  The T5
-bias table stays float32.  The oracle consumes these rounded values
-upcast to float64.
+bias table stays float32.  ALiBi slopes are not drawn: head h of H gets
+-2^(-8(h+1)/H) (a geometric set of distance penalties, float32).  The
+oracle consumes these rounded values upcast to float64.
 """
 
 from __future__ import annotations
@@ -25,7 +26,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "t5" | "shaw" | "deberta"
+    kind: str                 # "t5" | "shaw" | "deberta" | "alibi"
     B: int
     H: int
     Lq: int
@@ -54,6 +55,8 @@ class Workload:
         """Shapes of (table, table2) for this kind."""
         if self.kind == "t5":
             return (self.num_buckets, self.H), None
+        if self.kind == "alibi":
+            return (self.H,), None
         if self.kind == "shaw":
             n = 2 * self.clip_k + 1
             return (n, self.d), (n, self.d)
@@ -85,6 +88,11 @@ WORKLOADS = {
         description="T5 causal decode step: one query at position 4095 against "
                     "a cache whose first 1024 keys were evicted (keys at "
                     "positions 1024..4095), B4 H16 d64 bf16"),
+    "alibi_causal": Workload(
+        name="alibi_causal", kind="alibi", B=4, H=16, Lq=4096, Lk=4096, d=64,
+        dtype="bf16", causal=True,
+        description="ALiBi causal, slopes -2^(-8(h+1)/16) per head, B4 H16 "
+                    "L4096 d64 bf16"),
     "shaw_causal_k16": Workload(
         name="shaw_causal_k16", kind="shaw", B=4, H=16, Lq=4096, Lk=4096, d=64,
         dtype="bf16", clip_k=16, causal=True, table_sigma=0.1,
@@ -107,7 +115,10 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
     k = torch.randn(kshape, generator=g, dtype=torch.float32)
     v = torch.randn(kshape, generator=g, dtype=torch.float32)
     s1, s2 = wl.table_shapes()
-    table = torch.randn(s1, generator=g, dtype=torch.float32) * wl.table_sigma
+    if wl.kind == "alibi":
+        table = -torch.exp2(-8.0 * torch.arange(1, wl.H + 1, dtype=torch.float32) / wl.H)
+    else:
+        table = torch.randn(s1, generator=g, dtype=torch.float32) * wl.table_sigma
     table2 = None
     if s2 is not None:
         table2 = torch.randn(s2, generator=g, dtype=torch.float32) * wl.table_sigma
@@ -117,7 +128,7 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
         kv_valid_len = torch.randint(lo, hi + 1, (wl.B,), generator=g, dtype=torch.int32)
     dt = wl.torch_dtype
     q, k, v = q.to(dt), k.to(dt), v.to(dt)
-    if wl.kind != "t5":
+    if wl.kind in ("shaw", "deberta"):
         table = table.to(dt)
         table2 = table2.to(dt)
     return {"q": q, "k": k, "v": v, "table": table, "table2": table2,
