@@ -191,7 +191,7 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
                          bidirectional: bool = True, clip_k: int = 0,
                          q_pos_offset: int = 0, k_pos_offset: int = 0,
                          causal: bool = False, n_valid=None, scale=None,
-                         rows=None) -> np.ndarray:
+                         rows=None, return_lse: bool = False):
     """Forward pass of one (batch, head): q [Lq, d], k/v [Lk, d] -> [n, d].
 
     Steps (float64, everything materialised):
@@ -210,6 +210,8 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
       6. softmax over visible keys;
       7. output P V; Shaw adds sum_j p_ij a_V[row(i, j)] ([RPE] Shaw).
     ``rows`` selects query rows (all by default), for sampled comparisons.
+    ``return_lse`` also returns each row's log of the sum over visible keys
+    of exp(logit) (-inf for a row with no visible key).
     """
     if kind not in KINDS:
         raise ValueError(f"unknown kind {kind!r}")
@@ -269,6 +271,9 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
         mass = np.zeros((len(rows), a_v.shape[0]))
         np.add.at(mass, (np.arange(len(rows))[:, None].repeat(Lk, 1), idx["idx"]), p)
         out = out + mass @ a_v
+    if return_lse:
+        lse = np.where(any_visible, rowmax + np.log(np.where(any_visible, denom, 1.0)), -np.inf)
+        return out, lse
     return out
 
 
@@ -277,36 +282,35 @@ def relattn_forward(q, k, v, kind: str, table=None, table2=None, *,
                     bidirectional: bool = True, clip_k: int = 0,
                     q_pos_offset: int = 0, k_pos_offset: int = 0,
                     causal: bool = False, kv_valid_len=None, scale=None,
-                    heads=None, rows=None) -> np.ndarray:
+                    heads=None, rows=None, return_lse: bool = False):
     """Batched forward: q [B, H, Lq, d], k/v [B, H, Lk, d] -> float64.
 
     ``heads`` (list of (b, h)) and ``rows`` restrict the work for sampled
     comparisons; the result then has shape [len(heads), len(rows), d].
     Otherwise the result is [B, H, Lq, d].  Tables: T5 [num_buckets, H];
     Shaw a_K, a_V [2k+1, d]; DeBERTa Kr, Qr [2k, H, d]; ALiBi slopes [H].
+    ``return_lse`` also returns the row log-sum-exp ([B, H, Lq], or
+    [len(heads), len(rows)]).
     """
     q = np.asarray(q)
     B, H, Lq, d = q.shape
     kw = dict(num_buckets=num_buckets, max_distance=max_distance,
               bidirectional=bidirectional, clip_k=clip_k,
               q_pos_offset=q_pos_offset, k_pos_offset=k_pos_offset,
-              causal=causal, scale=scale, rows=rows)
+              causal=causal, scale=scale, rows=rows, return_lse=True)
     lens = None if kv_valid_len is None else np.asarray(kv_valid_len).reshape(-1)
-    if heads is None:
-        out = np.zeros((B, H, Lq, d), dtype=np.float64)
-        for b in range(B):
-            for h in range(H):
-                nv = None if lens is None else int(lens[b])
-                out[b, h] = relattn_forward_head(q[b, h], k[b, h], v[b, h], kind, h,
-                                                 table, table2, n_valid=nv, **kw)
-        return out
     n_rows = Lq if rows is None else len(rows)
-    out = np.zeros((len(heads), n_rows, d), dtype=np.float64)
-    for t, (b, h) in enumerate(heads):
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    out = np.zeros((len(pairs), n_rows, d), dtype=np.float64)
+    lse = np.zeros((len(pairs), n_rows), dtype=np.float64)
+    for t, (b, h) in enumerate(pairs):
         nv = None if lens is None else int(lens[b])
-        out[t] = relattn_forward_head(q[b, h], k[b, h], v[b, h], kind, h,
-                                      table, table2, n_valid=nv, **kw)
-    return out
+        out[t], lse[t] = relattn_forward_head(q[b, h], k[b, h], v[b, h], kind, h,
+                                              table, table2, n_valid=nv, **kw)
+    if heads is None:
+        out = out.reshape(B, H, n_rows, d)
+        lse = lse.reshape(B, H, n_rows)
+    return (out, lse) if return_lse else out
 
 
 # --------------------------------------------------------------------------

@@ -291,3 +291,46 @@ def test_alibi_steep_penalty_reads_the_key_at_distance_zero():
     q, k, v = _rand(rng, L, d), _rand(rng, L, d), _rand(rng, L, d)
     got = oracle.relattn_forward_head(q, k, v, "alibi", 0, np.array([-200.0]))
     np.testing.assert_allclose(got, v, atol=1e-12)
+
+
+# ------------------------------------------------------- row log-sum-exp
+
+def test_lse_equals_torch_logsumexp():
+    # zero tables: the logits are q.k * scale, so the row LSE is torch's
+    # logsumexp over the visible keys
+    rng = np.random.default_rng(24)
+    Lq, Lk, d = 9, 15, 8
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    mask = _mask_add(Lq, Lk, 3, True, 12)
+    logits = torch.from_numpy(q @ k.T / math.sqrt(d) + mask)
+    want = torch.logsumexp(logits, dim=1).numpy()
+    _, got = oracle.relattn_forward_head(q, k, v, "t5", 0, np.zeros((32, 1)), q_pos_offset=3,
+                                         causal=True, n_valid=12, return_lse=True)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+    _, none = oracle.relattn_forward_head(q, k, v, "t5", 0, np.zeros((32, 1)), n_valid=0,
+                                          return_lse=True)
+    assert np.all(np.isneginf(none))
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
+def test_two_key_segments_merge_by_lse(kind):
+    # keys split in two contiguous ranges, each placed by k_pos_offset: the
+    # two partial results merge exactly by their row LSE ([RPE] "Kernels and
+    # the KV cache": offset-only terms need no rewriting when a cache is cut)
+    rng = np.random.default_rng(25)
+    Lq, Lk, d, cut = 7, 20, 8, 9
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    t1, t2, kw = {"t5": (_rand(rng, 32, 1), None, {}),
+                  "shaw": (_rand(rng, 9, d), _rand(rng, 9, d), dict(clip_k=4)),
+                  "deberta": (_rand(rng, 10, 1, d), _rand(rng, 10, 1, d), dict(clip_k=5)),
+                  "alibi": (np.array([-0.3]), None, {})}[kind]
+    common = dict(q_pos_offset=13, causal=True, return_lse=True, **kw)
+    full, lf = oracle.relattn_forward_head(q, k, v, kind, 0, t1, t2, **common)
+    o1, l1 = oracle.relattn_forward_head(q, k[:cut], v[:cut], kind, 0, t1, t2, **common)
+    o2, l2 = oracle.relattn_forward_head(q, k[cut:], v[cut:], kind, 0, t1, t2,
+                                         k_pos_offset=cut, **common)
+    m = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - m), np.exp(l2 - m)
+    merged = (w1[:, None] * o1 + w2[:, None] * o2) / (w1 + w2)[:, None]
+    np.testing.assert_allclose(merged, full, atol=1e-12)
+    np.testing.assert_allclose(m + np.log(w1 + w2), lf, atol=1e-12)
