@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-/* 2: relattn_params gained k_pos_offset; kind RELATTN_ALIBI */
+/* 2: relattn_params gained k_pos_offset and lse; kind RELATTN_ALIBI */
 #define RELATTN_ABI_VERSION 2
 
 typedef enum {
@@ -125,8 +125,14 @@ typedef struct {
     int32_t k_pos_offset;    /* absolute position of key row 0 (>= 0)          */
     int32_t causal;          /* nonzero: hide keys after the query's position    */
     const int32_t *kv_valid_len; /* device int32 [B] or NULL: keys j >= len hidden */
-    float scale;             /* 0 = default: 1/sqrt(d) (T5, SHAW), 1/sqrt(3d)
+    float scale;             /* 0 = default: 1/sqrt(d) (T5, SHAW, ALIBI), 1/sqrt(3d)
                                 (DEBERTA)                                       */
+    float *lse;              /* device float32 [B, H, Lq] or NULL: written with
+                                log(sum over visible j of exp(s_ij)) (natural
+                                log), -inf for a row with no visible key.  Two
+                                calls over disjoint key ranges (k_pos_offset
+                                places each) merge exactly: out = (e^lse1 out1 +
+                                e^lse2 out2) / (e^lse1 + e^lse2)               */
 } relattn_params;
 
 /*

@@ -295,6 +295,93 @@ def test_parity_decode_one_token(wl):
 
 
 # ----------------------------------------------------------------------------
+# 2c. row log-sum-exp export and the merge of calls over disjoint key ranges
+# ----------------------------------------------------------------------------
+
+# bf16: the row sum is taken over P rounded to bfloat16 (round to nearest
+# even, at most 2^-8 relative per term), so |d ln(sum)| <= 2^-8 = 3.9e-3;
+# fp32 keeps the float32 sum
+LSE_TOL = {"fp32": 1e-5, "bf16": 4e-3}
+
+
+def _run_gpu_lse(wl, dev):
+    lse = torch.empty((wl.B, wl.H, wl.Lq), dtype=torch.float32, device=DEV)
+    out = ra.relattn_fwd(dev["q"], dev["k"], dev["v"], wl.kind, dev["table"], dev["table2"],
+                         kv_valid_len=dev["kv_valid_len"], lse=lse, **params_of(wl))
+    torch.cuda.synchronize()
+    return out, lse
+
+
+LSE_CASES = [c for c in SMALL_CASES if c.d == 64 or c.dtype == "fp32"][::3] + DECODE_CASES[::2]
+
+
+@pytest.mark.parametrize("wl", LSE_CASES, ids=_case_id)
+def test_lse_parity(wl):
+    inp = make_inputs(wl, seed=18)
+    out, lse = _run_gpu_lse(wl, _to_dev(inp))
+    want_o, want_l = oracle.relattn_forward(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), wl.kind,
+                                            _np(inp["table"]), _np(inp["table2"]),
+                                            kv_valid_len=None if inp["kv_valid_len"] is None
+                                            else inp["kv_valid_len"].numpy(),
+                                            return_lse=True, **params_of(wl))
+    check_close(out.cpu().float().numpy(), want_o, wl.dtype, _case_id(wl))
+    got_l = lse.cpu().numpy().astype(np.float64)
+    dead = np.isneginf(want_l)
+    assert np.array_equal(np.isneginf(got_l), dead)
+    err = np.abs(got_l[~dead] - want_l[~dead])
+    assert err.max() <= LSE_TOL[wl.dtype], err.max()
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
+def test_two_calls_over_a_cut_cache_merge_to_one(kind):
+    # a cache with a hole in the middle: keys at positions 0..399 and
+    # 700..1299, queries at 1250..1379; each segment is one call placed by
+    # k_pos_offset, and the two results merge by their row LSE
+    wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else (16 if kind == "shaw" else 512),
+             bidirectional=False, causal=True, Lq=130, Lk=1000, q_pos_offset=1250)
+    inp = make_inputs(wl, seed=19)
+    dev = _to_dev(inp)
+    seg = [(0, 400, 0), (400, 1000, 700)]
+    parts = []
+    for lo, hi, kpo in seg:
+        w = wl.replace(Lk=hi - lo, k_pos_offset=kpo)
+        d2 = dict(dev, k=dev["k"][:, :, lo:hi].contiguous(), v=dev["v"][:, :, lo:hi].contiguous())
+        parts.append(_run_gpu_lse(w, d2))
+    (o1, l1), (o2, l2) = parts
+    m = torch.maximum(l1, l2)
+    w1, w2 = torch.exp(l1 - m), torch.exp(l2 - m)
+    merged = (w1[..., None] * o1.float() + w2[..., None] * o2.float()) / (w1 + w2)[..., None]
+    # the oracle on the same cut cache: keys with their true positions
+    kpos = np.concatenate([np.arange(0, 400), np.arange(700, 1300)])
+    want = np.zeros((wl.B, wl.H, wl.Lq, wl.d))
+    for b in range(wl.B):
+        for h in range(wl.H):
+            o_a, la = oracle.relattn_forward_head(_np(inp["q"][b, h]), _np(inp["k"][b, h, :400]),
+                                                  _np(inp["v"][b, h, :400]), kind, h,
+                                                  _np(inp["table"]), _np(inp["table2"]),
+                                                  return_lse=True, **params_of(wl.replace(Lk=400)))
+            o_b, lb = oracle.relattn_forward_head(_np(inp["q"][b, h]), _np(inp["k"][b, h, 400:]),
+                                                  _np(inp["v"][b, h, 400:]), kind, h,
+                                                  _np(inp["table"]), _np(inp["table2"]),
+                                                  return_lse=True,
+                                                  **params_of(wl.replace(Lk=600, k_pos_offset=700)))
+            mm = np.maximum(la, lb)
+            wa, wb = np.exp(la - mm), np.exp(lb - mm)
+            want[b, h] = (wa[:, None] * o_a + wb[:, None] * o_b) / (wa + wb)[:, None]
+    assert kpos.size == wl.Lk
+    check_close(merged.cpu().numpy(), want, "bf16", kind)
+
+
+def test_lse_of_rows_without_keys_is_minus_inf():
+    wl = _kp("alibi", "bf16", 64, causal=True, Lq=120, Lk=200, q_pos_offset=300, k_pos_offset=350)
+    _, lse = _run_gpu_lse(wl, _to_dev(make_inputs(wl, seed=20)))
+    pos = 300 + np.arange(120)
+    got = lse.cpu().numpy()
+    assert np.all(np.isneginf(got[:, :, pos < 350]))
+    assert np.all(np.isfinite(got[:, :, pos >= 350]))
+
+
+# ----------------------------------------------------------------------------
 # 3. the five workloads at full size, in the benchmark's launch configuration;
 #    the oracle computes sampled (batch, head) pairs and query rows
 # ----------------------------------------------------------------------------

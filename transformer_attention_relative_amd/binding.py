@@ -39,6 +39,7 @@ class relattn_params(ctypes.Structure):
         ("q_pos_offset", ctypes.c_int32), ("k_pos_offset", ctypes.c_int32),
         ("causal", ctypes.c_int32),
         ("kv_valid_len", ctypes.c_void_p), ("scale", ctypes.c_float),
+        ("lse", ctypes.c_void_p),
     ]
 
 
@@ -96,11 +97,11 @@ def make_params(kind: str, dtype: str, B: int, H: int, Lq: int, Lk: int, d: int,
                 table=None, table2=None, num_buckets: int = 32, max_distance: int = 128,
                 bidirectional: bool = True, clip_k: int = 0, q_pos_offset: int = 0,
                 k_pos_offset: int = 0, causal: bool = False, kv_valid_len=None,
-                scale: float = 0.0) -> relattn_params:
+                scale: float = 0.0, lse=None) -> relattn_params:
     return relattn_params(
         KINDS[kind], DTYPES[dtype], B, H, Lq, Lk, d, _ptr(table), _ptr(table2),
         num_buckets, max_distance, int(bool(bidirectional)), clip_k, q_pos_offset,
-        k_pos_offset, int(bool(causal)), _ptr(kv_valid_len), float(scale))
+        k_pos_offset, int(bool(causal)), _ptr(kv_valid_len), float(scale), _ptr(lse))
 
 
 def _stream_handle(device) -> int:
@@ -118,7 +119,7 @@ def relattn_workspace_bytes(params: relattn_params) -> int:
 def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int = 32,
                 max_distance: int = 128, bidirectional: bool = True, clip_k: int = 0,
                 q_pos_offset: int = 0, k_pos_offset: int = 0, causal: bool = False,
-                kv_valid_len=None, scale: float = 0.0, out=None, workspace=None):
+                kv_valid_len=None, scale: float = 0.0, out=None, workspace=None, lse=None):
     """Fused forward on the current HIP stream; returns ``out``.
 
     q [B, H, Lq, d], k/v [B, H, Lk, d] (float32 or bfloat16, contiguous, on
@@ -128,7 +129,8 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
     absolute position ``q_pos_offset + i``, key row j at ``k_pos_offset + j``.
     ``kv_valid_len``:
     int32 [B] on the GPU or None.  ``out`` and ``workspace`` are allocated
-    with torch when not given.
+    with torch when not given.  ``lse``: a float32 [B, H, Lq] GPU tensor that
+    receives each row's log-sum-exp of the logits (natural log), or None.
     """
     import torch
     lib = load_library()
@@ -139,7 +141,7 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("q", q), ("k", k), ("v", v), ("table", table), ("table2", table2),
-                    ("kv_valid_len", kv_valid_len)):
+                    ("kv_valid_len", kv_valid_len), ("lse", lse)):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -148,13 +150,15 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
         raise TypeError("kv_valid_len must be int32")
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Lq)):
+        raise ValueError("lse must be a float32 [B, H, Lq] tensor")
     if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
         raise ValueError("k and v must be [B, H, Lk, d] matching q")
     p = make_params(kind, dtype, B, H, Lq, Lk, d, table=table, table2=table2,
                     num_buckets=num_buckets, max_distance=max_distance,
                     bidirectional=bidirectional, clip_k=clip_k, q_pos_offset=q_pos_offset,
                     k_pos_offset=k_pos_offset, causal=causal, kv_valid_len=kv_valid_len,
-                    scale=scale)
+                    scale=scale, lse=lse)
     if out is None:
         out = torch.empty_like(q)
     nbytes = relattn_workspace_bytes(p)

@@ -131,6 +131,8 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   if (!(p->scale >= 0.f) || std::isinf(p->scale))
     return fail(RELATTN_ERR_INVALID, "scale must be finite and >= 0 (0 = default)");
   if (!p->table) return fail(RELATTN_ERR_INVALID, "table is NULL");
+  if (p->lse && (reinterpret_cast<uintptr_t>(p->lse) & 3))
+    return fail(RELATTN_ERR_INVALID, "lse must be 4-byte aligned");
   if (p->kind == RELATTN_ALIBI && (reinterpret_cast<uintptr_t>(p->table) & 3))
     return fail(RELATTN_ERR_INVALID, "ALiBi slopes must be 4-byte aligned");
   if (p->kind == RELATTN_SHAW || p->kind == RELATTN_DEBERTA) {
@@ -286,6 +288,7 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.table = p->table; a.table2 = p->table2;
   a.kv_valid_len = p->kv_valid_len;
+  a.lse = p->lse;
   a.B = p->B; a.H = p->H; a.Lq = p->Lq; a.Lk = p->Lk;
   // the kernels see positions relative to key row 0 (may be negative)
   a.q_pos_offset = p->q_pos_offset - p->k_pos_offset;
@@ -316,7 +319,7 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
   e = launch_fwd(p->kind, P.bf, p->d, P.var, a, P.grid, P.lds, st);
   if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   if (P.n_splits > 1) {
-    CombineArgs cb{a.part_o, a.part_ml, out, p->B * p->H, p->Lq, P.n_splits};
+    CombineArgs cb{a.part_o, a.part_ml, out, p->lse, p->B * p->H, p->Lq, P.n_splits};
     e = launch_combine(P.bf, p->d, cb, st);
     if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   }

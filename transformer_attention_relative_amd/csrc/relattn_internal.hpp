@@ -35,6 +35,7 @@ struct FwdArgs {
   float *part_o;   // split-KV partial outputs  [n_splits][B*H][Lq][d]
   float *part_ml;  // split-KV row stats        [n_splits][B*H][Lq][2] (log2 max, sum)
   const void *colc; // DeBERTa per-key constants [B*H][Lk] x 8 bytes (relattn_colc_kernel)
+  float *lse;       // [B*H][Lq] row log-sum-exp (natural log) or NULL
   int32_t B, H, Lq, Lk;
   int32_t q_pos_offset;  // query row 0 minus key row 0 (absolute positions; may be < 0)
   int32_t causal;
@@ -67,6 +68,7 @@ struct ColcArgs {
 struct CombineArgs {
   const float *part_o, *part_ml;
   void *out;
+  float *lse;  // [BH][Lq] or NULL
   int32_t BH, Lq, n_splits;
 };
 

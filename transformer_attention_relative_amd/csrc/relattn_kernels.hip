@@ -670,11 +670,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
 
   // ---- per-kind prologue (LDS tables) ---------------------------------------
   float shaw_right[QB];                              // Shaw: q.(a_K[2k] - a_K[0])
+  float shaw_base[QB];                               // Shaw: q.a_K[0], left out of every logit
   float crow_lo[QB], crow_hi[QB];                    // DeBERTa: q.Kr[0], q.Kr[2k-1]
   T* arel = nullptr;     // Shaw: this wave's relative-key logits (input dtype)
   T* wbins = nullptr;    // Shaw: this wave's bin rows, [32 * QB][bin slots]
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = crow_lo[qb] = crow_hi[qb] = 0.f;
+  for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = shaw_base[qb] = crow_lo[qb] = crow_hi[qb] = 0.f;
 
   if constexpr (KIND == 0) {
     // four copies of bias[offset]/scale, copy c shifted by c entries:
@@ -718,6 +719,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         if (rb * 32 >= nrow) break;
         const f32x16 acc = mma_frag0<BF, D>(krow[rb], qf[qb]);
         if (rb == 0) base0 = __shfl(acc[0], lq);  // row 0 sits in lane lq, register 0
+        if (rb == 0) shaw_base[qb] = base0;
         // table rows past 2k land in the row's padding slot 2k+1
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -1316,7 +1318,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
         }
     }
     if (qrow[qb] >= a.Lq) continue;
+    // the row's reference on the logits' own scale (Shaw leaves q.a_K[0] out
+    // of every logit, a softmax-neutral shift)
+    const float m_row = KIND == 1 ? m_ref[qb] + c * shaw_base[qb] : m_ref[qb];
     if (a.n_splits == 1) {
+      // sum_j exp(logit_j) = l_tot * 2^m_row
+      if (a.lse != nullptr && hh == 0)
+        a.lse[(size_t)bh * a.Lq + qrow[qb]] =
+            l_tot > 0.f ? (__log2f(l_tot) + m_row) * 0.6931471805599453f : NEG_INF;
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       T* og = reinterpret_cast<T*>(a.out) + ((size_t)bh * a.Lq + qrow[qb]) * D;
 #pragma unroll
@@ -1347,7 +1356,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
           *reinterpret_cast<f32x4*>(po + dd) = y;
         }
       if (hh == 0) {
-        const f32x2 ml = {l_tot > 0.f ? m_ref[qb] : NEG_INF, l_tot};
+        const f32x2 ml = {l_tot > 0.f ? m_row : NEG_INF, l_tot};
         *reinterpret_cast<f32x2*>(a.part_ml + row * 2) = ml;
       }
     }
@@ -1395,6 +1404,8 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
     }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  if (a.lse != nullptr && ch == 0)
+    a.lse[row] = Lsum > 0.f ? (__log2f(Lsum) + M) * 0.6931471805599453f : RA_NEG_INF;
   T* og = reinterpret_cast<T*>(a.out) + row * D + 4 * ch;
   if constexpr (BF) {
     const bf16x2 y0 = cvt2(acc[0] * inv, acc[1] * inv), y1 = cvt2(acc[2] * inv, acc[3] * inv);
