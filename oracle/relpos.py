@@ -25,6 +25,13 @@ notes of the repository):
     removed, a fixed slope per head times the distance): bias = slope[h] *
     |key position - query position|, added after scaling like T5's bias;
     the slope carries its sign (negative slopes penalise distance).
+  * Transformer-XL ([RPE] "Transformer-XL: four terms and two global
+    biases"): logit = scale * ((q_i + u).k_j + (q_i + v).E[i - j]) with E the
+    projected relative encodings W_KR R(i - j) of one head, one row per
+    distance i - j >= 0 (table [rows, H, d]), u and v the global content and
+    position biases (table2 [2, H, d]); the whole sum is scaled by 1/sqrt(d)
+    as for Shaw.  It is causal (the memory segment precedes the queries) and
+    E must have a row for every visible distance.
   * Keys sit at absolute positions k_pos_offset + j; queries at
     q_pos_offset + i.  Padding masks key *index* j >= n_valid.
   * A row with no visible key has output 0.
@@ -41,7 +48,7 @@ import math
 
 import numpy as np
 
-KINDS = ("t5", "shaw", "deberta", "alibi")
+KINDS = ("t5", "shaw", "deberta", "alibi", "txl")
 
 
 # --------------------------------------------------------------------------
@@ -173,6 +180,8 @@ def rel_index_matrices(kind: str, Lq: int, Lk: int, *, q_pos_offset: int = 0,
                 "idx2": deberta_delta(key_minus_query, clip_k)}
     if kind == "alibi":
         return {"idx": np.abs(key_minus_query)}
+    if kind == "txl":
+        return {"idx": -key_minus_query}        # distance i - j, the row of E
     raise ValueError(f"unknown kind {kind!r}")
 
 
@@ -204,6 +213,9 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
          DeBERTa R[i, j] = (Q Kr_h^T)[i, delta(i,j)] + (K Qr_h^T)[j, delta(j,i)]
                                                 ([RPE] DeBERTa; [DRPE])
          ALiBi   bias[i, j] = slope[h] * distance    ([RPE] ALiBi and RoPE)
+         TXL     (q_i + u).k_j + (q_i + v).E[i - j]  ([RPE] Transformer-XL:
+                 (a)+(c) against content keys, (b)+(d) against the projected
+                 relative encodings)
       4. logits: T5 / ALiBi q.k*scale + bias; Shaw/DeBERTa (q.k + R)*scale;
       5. masks: causal hides keys after the query's position; padding hides
          key index j >= n_valid ([T5B]: masking is separate from bucketing);
@@ -238,6 +250,19 @@ def relattn_forward_head(q, k, v, kind: str, h: int, table=None, table2=None, *,
     elif kind == "alibi":
         slope = float(np.asarray(table, dtype=np.float64).reshape(-1)[h])
         logits = content * scale + slope * idx["idx"]
+    elif kind == "txl":
+        if not causal:
+            raise ValueError("Transformer-XL attention is causal")
+        enc = np.asarray(table, dtype=np.float64)[:, h, :]     # [rows, d]
+        u, vb = np.asarray(table2, dtype=np.float64)[:, h, :]  # [d] each
+        dist = idx["idx"]
+        vis = dist >= 0
+        if np.any(dist[vis] >= enc.shape[0]):
+            raise ValueError("relative encoding table too short for the visible distances")
+        terms_ac = (qr + u) @ k.T
+        pos_all = (qr + vb) @ enc.T                            # [n, rows]
+        terms_bd = np.take_along_axis(pos_all, np.clip(dist, 0, enc.shape[0] - 1), axis=1)
+        logits = (terms_ac + terms_bd) * scale
     elif kind == "shaw":
         a_k = np.asarray(table, dtype=np.float64)
         rel_keys = qr @ a_k.T                       # [n, 2k+1]
@@ -380,6 +405,12 @@ def relattn_forward_bruteforce(q, k, v, kind: str, h: int, table=None, table2=No
                 s = dot(q[i], k[j]) * scale + float(np.asarray(table)[b, h])
             elif kind == "alibi":
                 s = dot(q[i], k[j]) * scale + float(np.asarray(table).reshape(-1)[h]) * abs(pj - pi)
+            elif kind == "txl":
+                enc_row = list(map(float, np.asarray(table, dtype=np.float64)[pi - pj, h]))
+                u = list(map(float, np.asarray(table2, dtype=np.float64)[0, h]))
+                vb = list(map(float, np.asarray(table2, dtype=np.float64)[1, h]))
+                s = (dot([a + b for a, b in zip(q[i], u)], k[j])
+                     + dot([a + b for a, b in zip(q[i], vb)], enc_row)) * scale
             elif kind == "shaw":
                 s = dot(q[i], [a + b for a, b in zip(k[j], pair_key[i][j])]) * scale
             else:

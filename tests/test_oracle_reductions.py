@@ -211,7 +211,7 @@ def test_rows_selection_matches_full():
 # -------------------------------------------------------------- brute force
 
 @settings(max_examples=60, deadline=None)
-@given(kind=st.sampled_from(["t5", "shaw", "deberta", "alibi"]),
+@given(kind=st.sampled_from(["t5", "shaw", "deberta", "alibi", "txl"]),
        Lq=st.integers(1, 9), Lk=st.integers(1, 12), d=st.sampled_from([2, 4, 8]),
        q_off=st.integers(0, 40), k_off=st.integers(0, 40), causal=st.booleans(),
        bidir=st.booleans(), nb=st.sampled_from([4, 8, 16, 32, 64]),
@@ -229,6 +229,10 @@ def test_vectorised_equals_bruteforce(kind, Lq, Lk, d, q_off, k_off, causal, bid
         t1, t2 = _rand(rng, nb, H), None
     elif kind == "alibi":
         t1, t2 = _rand(rng, H, s=0.3), None
+    elif kind == "txl":
+        causal = True
+        rows = max(1, q_off + Lq - k_off)
+        t1, t2 = _rand(rng, rows, H, d), _rand(rng, 2, H, d)
     elif kind == "shaw":
         t1, t2 = _rand(rng, 2 * clip + 1, d), _rand(rng, 2 * clip + 1, d)
     else:
@@ -334,3 +338,60 @@ def test_two_key_segments_merge_by_lse(kind):
     merged = (w1[:, None] * o1 + w2[:, None] * o2) / (w1 + w2)[:, None]
     np.testing.assert_allclose(merged, full, atol=1e-12)
     np.testing.assert_allclose(m + np.log(w1 + w2), lf, atol=1e-12)
+
+
+# --------------------------------------------------------- Transformer-XL
+
+def test_txl_position_terms_equal_the_skew():
+    # [RPE] Transformer-XL: terms (b)+(d) are (q_i + v) against the projected
+    # relative encodings "followed by the same skew".  With content keys at
+    # zero only those terms remain; the page's pad / reshape / slice of
+    # (Q + v) E_s^T, E_s[r] = the encoding of key - query = r - (L - 1), gives
+    # the same causal logits as the oracle's gather by distance i - j.
+    rng = np.random.default_rng(31)
+    L, d, H, h = 9, 8, 2, 1
+    q, v = _rand(rng, L, d), _rand(rng, L, d)
+    k = np.zeros((L, d))
+    enc = _rand(rng, L, H, d)                  # enc[r] encodes distance i - j = r
+    uv = _rand(rng, 2, H, d)
+    e_skew = enc[::-1, h, :]                   # row r <-> i - j = L - 1 - r
+    s = oracle.skew((q + uv[1, h]) @ e_skew.T) / math.sqrt(d)
+    mask = np.where(np.tril(np.ones((L, L))) > 0, s, -np.inf)
+    want = _sdpa(q, k, v, mask, 1 / math.sqrt(d))
+    got = oracle.relattn_forward_head(q, k, v, "txl", h, enc, uv, causal=True)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+def test_txl_content_bias_is_a_per_key_term():
+    # E = 0 and v = 0: only (q_i + u).k_j remains, i.e. plain attention plus
+    # scale * u.k_j for every row, as a dense mask through torch's attention
+    rng = np.random.default_rng(32)
+    Lq, Lk, d, H = 7, 12, 8, 1
+    q, k, v = _rand(rng, Lq, d), _rand(rng, Lk, d), _rand(rng, Lk, d)
+    uv = np.zeros((2, H, d))
+    uv[0, 0] = _rand(rng, d)
+    kpos, qpos = np.arange(Lk)[None, :], 5 + np.arange(Lq)[:, None]
+    mask = np.where(kpos <= qpos, np.broadcast_to((k @ uv[0, 0]) / math.sqrt(d), (Lq, Lk)), -np.inf)
+    want = _sdpa(q, k, v, mask, 1 / math.sqrt(d))
+    got = oracle.relattn_forward_head(q, k, v, "txl", 0, np.zeros((Lk + 5, H, d)), uv,
+                                      q_pos_offset=5, causal=True)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+    # and with u = 0 as well: plain causal attention
+    got0 = oracle.relattn_forward_head(q, k, v, "txl", 0, np.zeros((Lk + 5, H, d)),
+                                       np.zeros((2, H, d)), q_pos_offset=5, causal=True)
+    want0 = _sdpa(q, k, v, np.where(kpos <= qpos, 0.0, -np.inf), 1 / math.sqrt(d))
+    np.testing.assert_allclose(got0, want0, atol=1e-12)
+
+
+def test_txl_shift_and_table_checks():
+    rng = np.random.default_rng(33)
+    q, k, v = _rand(rng, 6, 8), _rand(rng, 10, 8), _rand(rng, 10, 8)
+    enc, uv = _rand(rng, 12, 1, 8), _rand(rng, 2, 1, 8)
+    a = oracle.relattn_forward_head(q, k, v, "txl", 0, enc, uv, q_pos_offset=4, causal=True)
+    b = oracle.relattn_forward_head(q, k, v, "txl", 0, enc, uv, q_pos_offset=504,
+                                    k_pos_offset=500, causal=True)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.relattn_forward_head(q, k, v, "txl", 0, enc, uv, q_pos_offset=4)   # not causal
+    with pytest.raises(ValueError):
+        oracle.relattn_forward_head(q, k, v, "txl", 0, enc[:5], uv, q_pos_offset=4, causal=True)
