@@ -36,7 +36,7 @@ from transformer_attention_relative_amd.synthetic import WORKLOADS, Workload, ma
 
 DEFAULT_WORKLOAD = "t5_encoder_padded"
 SECONDARY = ["t5_decoder_kvcache", "t5_decode_evicted", "shaw_causal_k16", "deberta_k512",
-             "alibi_causal"]
+             "alibi_causal", "txl_memory"]
 METRIC = "rel-pos attention fwd TFLOP/s and % of MFMA bf16 peak (1 MI355X)"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0                             # MI355X published HBM3E bandwidth
@@ -76,6 +76,9 @@ def counted_work(wl: Workload, kv_valid_len):
             lo = np.clip(-pos, -k, k)
             hi = np.clip(nvis - 1 - pos, -k, k)
             per_head += 4.0 * wl.d * np.where(has, hi - lo + 1, 0).sum()
+        elif wl.kind == "txl":
+            # (q + v).E[i - j]: one distinct (row, distance) per visible pair
+            per_head += 2.0 * wl.d * nvis.sum()
         elif wl.kind == "deberta":
             has = nvis > 0
             hi = np.clip(pos, -k, k - 1)
@@ -105,6 +108,8 @@ def counted_work(wl: Workload, kv_valid_len):
         tab = 2 * (2 * k + 1) * wl.d * esz
     elif wl.kind == "alibi":
         tab = wl.H * 4
+    elif wl.kind == "txl":
+        tab = (k + 2) * wl.H * wl.d * esz
     else:
         tab = 2 * (2 * k) * wl.H * wl.d * esz
     return flops, qo_bytes + kv_bytes + tab

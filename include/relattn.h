@@ -35,6 +35,14 @@
  *           removed: a fixed slope per head times the distance, no maximum
  *           distance).  The slope carries its sign: a negative slope
  *           penalises distance.
+ *   TXL     s_ij = scale * ((q_i + u_h).k_j + (q_i + v_h).E[p_i - t_j, h]),
+ *           value_ij = v_j.  [RPE] "Transformer-XL: four terms and two global
+ *           biases": content keys against the query plus the global content
+ *           bias u, projected relative encodings E = W_KR R(i - j) against
+ *           the query plus the global position bias v.  Causal only (the
+ *           cached segment precedes the queries); E has one row per distance
+ *           0 .. clip_k - 1 and must cover every visible distance.  The sums
+ *           q + u and q + v are rounded to the input type.
  *
  * Offset conventions (documented because mixing them swaps past and future,
  * [RPE] "Failure modes"): T5 and Shaw index by key - query; DeBERTa's
@@ -77,14 +85,15 @@
 extern "C" {
 #endif
 
-/* 2: relattn_params gained k_pos_offset and lse; kind RELATTN_ALIBI */
+/* 2: relattn_params gained k_pos_offset and lse; kinds RELATTN_ALIBI, RELATTN_TXL */
 #define RELATTN_ABI_VERSION 2
 
 typedef enum {
     RELATTN_T5 = 0,
     RELATTN_SHAW = 1,
     RELATTN_DEBERTA = 2,
-    RELATTN_ALIBI = 3
+    RELATTN_ALIBI = 3,
+    RELATTN_TXL = 4
 } relattn_kind;
 
 typedef enum {
@@ -108,6 +117,8 @@ typedef enum {
  *           shared by all heads ([RPE] Shaw section)
  *   DEBERTA table  : Kr [2*clip_k, H, d] (dtype)    table2 : Qr, same shape
  *   ALIBI   table  : float32 slopes [H]             table2 : unused (NULL)
+ *   TXL     table  : E [clip_k, H, d] (dtype)       table2 : [2, H, d] (dtype):
+ *           row 0 = u, row 1 = v
  * Device pointers must be 16-byte aligned (ALiBi slopes: 4-byte).
  */
 typedef struct {
@@ -119,7 +130,8 @@ typedef struct {
     int32_t num_buckets;     /* T5: total buckets (2..256)                       */
     int32_t max_distance;    /* T5: distance where log buckets end (> exact range) */
     int32_t bidirectional;   /* T5: nonzero = split buckets by direction         */
-    int32_t clip_k;          /* SHAW (1..32) / DEBERTA (1..65536): clip k        */
+    int32_t clip_k;          /* SHAW (1..32) / DEBERTA (1..65536): clip k;
+                                TXL: rows of the relative encodings E          */
     int32_t q_pos_offset;    /* absolute position of query row 0 (>= 0)
                                 ([T5B], cached decoder)                         */
     int32_t k_pos_offset;    /* absolute position of key row 0 (>= 0)          */
@@ -156,7 +168,8 @@ relattn_status relattn_workspace_bytes(const relattn_params *p, size_t *bytes);
  * Relative index of n (query position, key position) pairs, computed by the
  * same device index functions the fused kernel uses:
  *   which = 0: T5 bucket(k_pos - q_pos) | SHAW clip(k_pos - q_pos, -k, k) + k |
- *              DEBERTA d(q_pos, k_pos) | ALIBI |k_pos - q_pos|
+ *              DEBERTA d(q_pos, k_pos) | ALIBI |k_pos - q_pos| |
+ *              TXL q_pos - k_pos (the row of E)
  *   which = 1: DEBERTA d(k_pos, q_pos) (position-to-content index); other
  *              kinds reject it.
  * Only kind and the kind's index parameters of *p are read (shapes and

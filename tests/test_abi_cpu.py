@@ -84,6 +84,10 @@ def _fwd_status(lib, p):
     (dict(kind="shaw", table=FAKE, table2=FAKE, clip_k=33), 2),
     (dict(kind="deberta", table=FAKE, table2=FAKE, clip_k=0), 1),
     (dict(kind="deberta", table=FAKE, table2=_FakeTensor(0x10004), clip_k=4), 1),  # misaligned
+    (dict(kind="txl", table=FAKE, table2=FAKE, clip_k=64), 1),                     # not causal
+    (dict(kind="txl", table=FAKE, table2=FAKE, clip_k=63, causal=True), 1),        # E too short
+    (dict(kind="alibi", table=_FakeTensor(0x10002)), 1),                           # misaligned slopes
+    (dict(kind="t5", table=FAKE, lse=_FakeTensor(0x10002)), 1),                    # misaligned lse
     (dict(kind="t5", table=FAKE), 1),                       # valid params, NULL tensors
 ])
 def test_fwd_validation_rejects_before_launch(lib, kw, status):

@@ -133,6 +133,10 @@ for dtype in ("fp32", "bf16"):
             _small("alibi", dtype, d),
             _small("alibi", dtype, d, causal=True, Lq=333),
             _small("alibi", dtype, d, causal=True, Lq=200, q_pos_offset=133, valid_len_range=(1, 333)),
+            # Transformer-XL: a segment after a memory of 203 keys
+            _small("txl", dtype, d, causal=True, Lq=130, q_pos_offset=203, clip_k=333),
+            _small("txl", dtype, d, causal=True, Lq=300, q_pos_offset=33, clip_k=400,
+                   valid_len_range=(50, 333)),
         ]
 
 
@@ -219,6 +223,7 @@ for dtype, d in (("bf16", 64), ("fp32", 32)):
             k_pos_offset=350),
         _kp("alibi", dtype, d, causal=True, q_pos_offset=2000, k_pos_offset=1700),
         _kp("alibi", dtype, d, Lq=200, Lk=250, q_pos_offset=0, k_pos_offset=300),
+        _kp("txl", dtype, d, causal=True, q_pos_offset=2000, k_pos_offset=1700, clip_k=430),
     ]
 
 
@@ -234,20 +239,24 @@ def test_parity_key_positions(wl):
         assert not np.any(got[:, :, dead])
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
+def _clip_for(kind, dflt, txl_rows):
+    return 0 if kind in ("t5", "alibi") else (txl_rows if kind == "txl" else dflt)
+
+
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi", "txl"])
 def test_keys_all_ahead_of_queries_give_zeros(kind):
-    wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else 8, bidirectional=False,
+    wl = _kp(kind, "bf16", 64, clip_k=_clip_for(kind, 8, 1), bidirectional=False,
              causal=True, Lq=64, Lk=100, q_pos_offset=10, k_pos_offset=74)
     got = run_gpu(wl, _to_dev(make_inputs(wl, seed=14))).cpu()
     assert torch.count_nonzero(got) == 0
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi", "txl"])
 def test_shifting_both_positions_changes_nothing(kind):
     # every term depends on key position - query position only ([RPE]:
     # shifting the input by a constant must leave the output unchanged), so
     # the kernels see identical inputs and the outputs are bit-identical
-    wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else 12, bidirectional=False,
+    wl = _kp(kind, "bf16", 64, clip_k=_clip_for(kind, 12, 300), bidirectional=False,
              causal=True, Lq=150, Lk=300, q_pos_offset=200, k_pos_offset=60)
     dev = _to_dev(make_inputs(wl, seed=15))
     a = run_gpu(wl, dev).clone()
@@ -267,6 +276,8 @@ DECODE1_CASES = [
              clip_k=512, causal=True, q_pos_offset=1600, k_pos_offset=100, table_sigma=0.1),
     Workload(name="dec1", kind="alibi", B=2, H=8, Lq=1, Lk=3000, d=64, dtype="bf16",
              causal=True, q_pos_offset=3999, k_pos_offset=1000),
+    Workload(name="dec1", kind="txl", B=2, H=4, Lq=1, Lk=3000, d=64, dtype="bf16",
+             causal=True, q_pos_offset=2999, clip_k=3000, table_sigma=0.1),
 ]
 
 
@@ -332,12 +343,12 @@ def test_lse_parity(wl):
     assert err.max() <= LSE_TOL[wl.dtype], err.max()
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi", "txl"])
 def test_two_calls_over_a_cut_cache_merge_to_one(kind):
     # a cache with a hole in the middle: keys at positions 0..399 and
     # 700..1299, queries at 1250..1379; each segment is one call placed by
     # k_pos_offset, and the two results merge by their row LSE
-    wl = _kp(kind, "bf16", 64, clip_k=0 if kind == "t5" else (16 if kind == "shaw" else 512),
+    wl = _kp(kind, "bf16", 64, clip_k={"shaw": 16, "deberta": 512, "txl": 1380}.get(kind, 0),
              bidirectional=False, causal=True, Lq=130, Lk=1000, q_pos_offset=1250)
     inp = make_inputs(wl, seed=19)
     dev = _to_dev(inp)
@@ -422,13 +433,13 @@ def test_deterministic(name):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi"])
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi", "txl"])
 def test_masked_keys_do_not_matter(kind):
     # [T5B]: check masking on its own -- perturbing keys that are hidden
     # (padding, or after the query under the causal mask) leaves the output
     # bit-identical.
     wl = _small(kind, "bf16", 64, causal=True, Lq=200, Lk=333, q_pos_offset=100,
-                valid_len_range=(150, 280), clip_k=8 if kind != "t5" else 0,
+                valid_len_range=(150, 280), clip_k=_clip_for(kind, 8, 300),
                 bidirectional=False)
     inp = make_inputs(wl, seed=3)
     dev = _to_dev(inp)

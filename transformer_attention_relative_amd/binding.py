@@ -16,7 +16,7 @@ from typing import Optional
 
 from .build import LIB_PATH
 
-KINDS = {"t5": 0, "shaw": 1, "deberta": 2, "alibi": 3}
+KINDS = {"t5": 0, "shaw": 1, "deberta": 2, "alibi": 3, "txl": 4}
 DTYPES = {"fp32": 0, "bf16": 1}
 STATUS = {0: "RELATTN_OK", 1: "RELATTN_ERR_INVALID", 2: "RELATTN_ERR_UNSUPPORTED",
           3: "RELATTN_ERR_WORKSPACE", 4: "RELATTN_ERR_HIP"}
@@ -125,7 +125,8 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
     q [B, H, Lq, d], k/v [B, H, Lk, d] (float32 or bfloat16, contiguous, on
     the GPU).  Tables: T5 float32 [num_buckets, H]; Shaw a_K / a_V
     [2k+1, d]; DeBERTa Kr / Qr [2k, H, d] (input dtype); ALiBi float32
-    slopes [H].  Query row i sits at
+    slopes [H]; Transformer-XL encodings E [clip_k, H, d] and (u, v)
+    [2, H, d] (input dtype).  Query row i sits at
     absolute position ``q_pos_offset + i``, key row j at ``k_pos_offset + j``.
     ``kv_valid_len``:
     int32 [B] on the GPU or None.  ``out`` and ``workspace`` are allocated

@@ -111,7 +111,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 relattn_status plan_problem(const relattn_params* p, Plan* P) {
   if (!p) return fail(RELATTN_ERR_INVALID, "params is NULL");
-  if (p->kind < 0 || p->kind > 3) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
+  if (p->kind < 0 || p->kind > 4) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
   if (p->dtype != RELATTN_FP32 && p->dtype != RELATTN_BF16)
     return fail(RELATTN_ERR_INVALID, "unknown dtype %d", p->dtype);
   if (p->B < 1 || p->H < 1 || p->Lq < 1 || p->Lk < 1)
@@ -135,7 +135,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     return fail(RELATTN_ERR_INVALID, "lse must be 4-byte aligned");
   if (p->kind == RELATTN_ALIBI && (reinterpret_cast<uintptr_t>(p->table) & 3))
     return fail(RELATTN_ERR_INVALID, "ALiBi slopes must be 4-byte aligned");
-  if (p->kind == RELATTN_SHAW || p->kind == RELATTN_DEBERTA) {
+  if (p->kind == RELATTN_SHAW || p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) {
     if (!p->table2) return fail(RELATTN_ERR_INVALID, "table2 is NULL");
     if (!aligned16(p->table) || !aligned16(p->table2))
       return fail(RELATTN_ERR_INVALID, "tables must be 16-byte aligned");
@@ -144,6 +144,14 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
       return fail(RELATTN_ERR_UNSUPPORTED, "Shaw clip_k=%d above %d", p->clip_k, kShawMaxK);
     if (p->kind == RELATTN_DEBERTA && p->clip_k > 65536)
       return fail(RELATTN_ERR_UNSUPPORTED, "DeBERTa clip_k=%d above 65536", p->clip_k);
+  }
+  if (p->kind == RELATTN_TXL) {
+    // causal, and a relative-encoding row for every distance a query can see
+    if (!p->causal) return fail(RELATTN_ERR_INVALID, "Transformer-XL attention must be causal");
+    const int64_t far = (int64_t)p->q_pos_offset + p->Lq - 1 - p->k_pos_offset;
+    if (far >= p->clip_k)
+      return fail(RELATTN_ERR_INVALID, "Transformer-XL encodings have %d rows; distances up to %lld are visible",
+                  p->clip_k, (long long)far);
   }
   P->bf = p->dtype == RELATTN_BF16;
   const float dflt = p->kind == RELATTN_DEBERTA ? 1.f / std::sqrt(3.f * p->d) : 1.f / std::sqrt((float)p->d);
@@ -171,7 +179,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   };
   Variant var = Variant{4, 1};
   int lds_total = 0, lut_n = 0;
-  if (p->kind != RELATTN_DEBERTA && P->bf) {
+  if ((p->kind == RELATTN_T5 || p->kind == RELATTN_SHAW || p->kind == RELATTN_ALIBI) && P->bf) {
     const int64_t wgs2 = (int64_t)BH * ((p->Lq + 4 * 64 - 1) / (4 * 64));
     int t2 = 0;
     if (wgs2 >= 2 * kNumCU && lds_for(Variant{4, 2}, &t2, &lut_n) == RELATTN_OK &&
@@ -329,7 +337,7 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
 relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, const int32_t* k_pos,
                                  int64_t n, int32_t which, int32_t* idx_out, void* stream) {
   if (!p) return fail(RELATTN_ERR_INVALID, "params is NULL");
-  if (p->kind < 0 || p->kind > 3) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
+  if (p->kind < 0 || p->kind > 4) return fail(RELATTN_ERR_INVALID, "unknown kind %d", p->kind);
   if (n < 0) return fail(RELATTN_ERR_INVALID, "n=%lld < 0", (long long)n);
   if (which != 0 && which != 1) return fail(RELATTN_ERR_INVALID, "which=%d not 0 or 1", which);
   if (which == 1 && p->kind != RELATTN_DEBERTA)
@@ -343,7 +351,7 @@ relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, 
     a.t5_slots = P.slots; a.t5_exact = P.exact; a.t5_bidir = p->bidirectional ? 1 : 0;
     a.t5_nthr = P.nthr;
     for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.nthr ? P.thr[m] : INT32_MAX;
-  } else if (p->kind != RELATTN_ALIBI) {
+  } else if (p->kind == RELATTN_SHAW || p->kind == RELATTN_DEBERTA) {
     if (p->clip_k < 1) return fail(RELATTN_ERR_INVALID, "clip_k=%d must be >= 1", p->clip_k);
   }
   if (n == 0) return ok();

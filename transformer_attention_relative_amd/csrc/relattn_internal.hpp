@@ -107,6 +107,7 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //           row of the wave; bf16 only: a_V^T [d][bin_slots]
 //   DEBERTA per wave: float band[32][kCbandStride], the content-to-position
 //           band [query][m] and then the position-to-content band [key][n]
+//   TXL     per wave: float band[32][kCbandStride], the position band [query][m]
 constexpr int kCbandStride = 68;  // 64 band columns, padded: rows stay 16-byte aligned and
                                   // a query's diagonal (stride 69) hits distinct banks
 
@@ -141,7 +142,7 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     L.wscr_wave_bytes = rows * shaw_bin_stride(clip_k, esz) * esz;
     L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
     rel_bytes = L.avt_off + (bf16 ? d * nbin * 2 : 0);
-  } else if (kind == 2) {
+  } else if (kind == 2 || kind == 4) {
     L.deb_wave_floats = kBlockRows * kCbandStride;
     rel_bytes = nw * L.deb_wave_floats * 4;
   }  // ALIBI: nothing beyond the stages

@@ -125,6 +125,8 @@ __global__ void relattn_index_kernel(IndexArgs a) {
       r = shaw_row_dev(kp - qp, a.clip_k);
     } else if (a.kind == 3) {
       r = abs(kp - qp);  // ALiBi distance
+    } else if (a.kind == 4) {
+      r = qp - kp;       // Transformer-XL: row of the relative encodings
     } else {
       r = a.which == 0 ? deberta_delta_dev(qp - kp, a.clip_k) : deberta_delta_dev(kp - qp, a.clip_k);
     }
@@ -452,6 +454,24 @@ __device__ __forceinline__ float ref_offset(float cb, float m_ref) {
 // constants come from relattn_colc_kernel (float32 dot products) and enter
 // the score accumulator through one MFMA: A holds the key's constants (as
 // bfloat16 hi + lo pairs, or float32), B selects the side for every query.
+// a + b elementwise, rounded to the fragment's element type
+template <int D>
+__device__ __forceinline__ TableFrag<true, D> frag_add(const TableFrag<true, D>& x, const TableFrag<true, D>& y) {
+  TableFrag<true, D> r;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.v[t][e] = (bf16)((float)x.v[t][e] + (float)y.v[t][e]);
+  return r;
+}
+template <int D>
+__device__ __forceinline__ TableFrag<false, D> frag_add(const TableFrag<false, D>& x, const TableFrag<false, D>& y) {
+  TableFrag<false, D> r;
+#pragma unroll
+  for (int t = 0; t < D / 2; ++t) r.v[t] = x.v[t] + y.v[t];
+  return r;
+}
+
 template <bool BF>
 struct KeyConst;
 template <>
@@ -659,6 +679,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
     alibi_s = reinterpret_cast<const float*>(a.table)[h] / a.scale;
     alibi_kc.set(-alibi_s * (float)lq, alibi_s * (float)lq, hh);
   }
+  // Transformer-XL: the query plus the global content bias u (against the
+  // content keys) and plus the global position bias v (against the
+  // relative encodings), each rounded to the input type
+  QFrag qv[KIND == 4 ? QB : 1];
+  if constexpr (KIND == 4) {
+    const T* uv = reinterpret_cast<const T*>(a.table2);
+    QFrag uf, vf;
+    uf.load(uv + (size_t)h * D, hh);
+    vf.load(uv + ((size_t)a.H + h) * D, hh);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      qv[qb] = frag_add<D>(qf[qb], vf);
+      qf[qb] = frag_add<D>(qf[qb], uf);
+    }
+  }
 
   const int kv_lim = max(0, min(a.Lk, kv_valid));
   const int kv_end = min(kv_lim, causal_end);
@@ -860,7 +895,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       if constexpr (KIND == 0) far = omax <= -a.t5_lsat || omin >= a.t5_rsat;
       else if constexpr (KIND == 1) far = omin >= ck || omax <= -ck;
       else if constexpr (KIND == 2) far = -omax >= ck || -omin <= -ck;
-      else far = omax <= 0 || omin >= 0;  // ALiBi: every key on one side
+      else if constexpr (KIND == 3) far = omax <= 0 || omin >= 0;  // ALiBi: every key on one side
+      else far = false;  // Transformer-XL: the encodings are never clipped
       far_all = far_all && far;
       near_all = near_all && !far;
     }
@@ -935,7 +971,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       } else if constexpr (KIND == 2) {
         if (-omax >= ck) { deb_side[qb] = 0; b_tile[qb] = crow_hi[qb]; }       // every query - key >= k
         else if (-omin <= -ck) { deb_side[qb] = 1; b_tile[qb] = crow_lo[qb]; } // every query - key <= -k
-      } else {
+      } else if constexpr (KIND == 3) {
         if (omax <= 0) deb_side[qb] = 0;       // every key at or before every query
         else if (omin >= 0) deb_side[qb] = 1;  // every key at or after every query
       }
@@ -1031,6 +1067,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
             for (int i = 0; i < 16; ++i) init[i] = alibi_s * (float)abs(obase + acc_row(i, 0));
             s = mma_frag<BF, D>(kf, qf[qb], init);
           }
+        } else if constexpr (KIND == 4) {
+          // (q + v).E[i - j] for the block's 63 distances by MFMA (rows
+          // E[T0 + m], columns = queries), stored [query][m] in the wave's
+          // LDS tile and read back along each query's diagonal
+          float* band = relf + wave * L.deb_wave_floats;
+          const T* enc = reinterpret_cast<const T*>(a.table);
+          const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
+          TableFrag<BF, D> ef[2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)  // negative distances are hidden keys: any row serves
+            ef[tb].load(enc + ((size_t)min(max(T0 + 32 * tb + lq, 0), ck - 1) * a.H + h) * D, hh);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const f32x16 acc = mma_frag0<BF, D>(ef[tb], qv[qb]);
+            float* dst = band + lq * kCbandStride + 32 * tb + 4 * hh;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+              *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
+            }
+          }
+          wave_lds_fence();
+          f32x16 init;
+          {
+            const float* crow = band + lq * (kCbandStride + 1) + 31;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) init[i] = crow[-acc_row(i, hh)];
+          }
+          wave_lds_fence();  // the next block overwrites the tile
+          s = mma_frag<BF, D>(kf, qf[qb], init);
         } else {
           const int side = CLS == 0 ? deb_side[qb] : deb_block_side(qb);
           if (side >= 0) {
@@ -1471,7 +1537,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 }
 
 bool fwd_variant_built(int kind, bool bf, Variant v) {
-  if (kind == 2) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
+  if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
 
@@ -1483,7 +1549,7 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
 #define RA_DT(K, QBV, NWV)                                                        \
   RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
   RA_CASE(K, false, 32, QBV, NWV)
-  RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4)
+  RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4) RA_DT(4, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
   RA_CASE(1, true, 64, 2, 4) RA_CASE(1, true, 32, 2, 4)
   RA_CASE(3, true, 64, 2, 4) RA_CASE(3, true, 32, 2, 4)

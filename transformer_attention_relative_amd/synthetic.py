@@ -26,7 +26,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "t5" | "shaw" | "deberta" | "alibi"
+    kind: str                 # "t5" | "shaw" | "deberta" | "alibi" | "txl"
     B: int
     H: int
     Lq: int
@@ -57,6 +57,8 @@ class Workload:
             return (self.num_buckets, self.H), None
         if self.kind == "alibi":
             return (self.H,), None
+        if self.kind == "txl":
+            return (self.clip_k, self.H, self.d), (2, self.H, self.d)
         if self.kind == "shaw":
             n = 2 * self.clip_k + 1
             return (n, self.d), (n, self.d)
@@ -81,6 +83,12 @@ WORKLOADS = {
         q_pos_offset=3968, causal=True, table_sigma=0.5,
         description="T5 causal decoder with KV cache: 128 queries at positions "
                     "3968..4095 against keys 0..4095, B4 H16 d64 bf16"),
+    "txl_memory": Workload(
+        name="txl_memory", kind="txl", B=4, H=16, Lq=2048, Lk=4096, d=64, dtype="bf16",
+        clip_k=4096, q_pos_offset=2048, causal=True, table_sigma=0.1,
+        description="Transformer-XL: a 2048-token segment at positions 2048..4095 "
+                    "attending to itself and a 2048-token memory, encodings "
+                    "E [4096,16,64] and u, v [2,16,64] ~N(0,0.1), B4 H16 d64 bf16"),
     "t5_decode_evicted": Workload(
         name="t5_decode_evicted", kind="t5", B=4, H=16, Lq=1, Lk=3072, d=64,
         dtype="bf16", num_buckets=32, max_distance=128, bidirectional=False,
@@ -128,7 +136,7 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
         kv_valid_len = torch.randint(lo, hi + 1, (wl.B,), generator=g, dtype=torch.int32)
     dt = wl.torch_dtype
     q, k, v = q.to(dt), k.to(dt), v.to(dt)
-    if wl.kind in ("shaw", "deberta"):
+    if wl.kind in ("shaw", "deberta", "txl"):
         table = table.to(dt)
         table2 = table2.to(dt)
     return {"q": q, "k": k, "v": v, "table": table, "table2": table2,
