@@ -36,7 +36,7 @@ from transformer_attention_relative_amd.synthetic import WORKLOADS, Workload, ma
 
 DEFAULT_WORKLOAD = "t5_encoder_padded"
 SECONDARY = ["t5_decoder_kvcache", "t5_decode_evicted", "shaw_causal_k16", "deberta_k512",
-             "alibi_causal", "txl_memory"]
+             "alibi_causal", "alibi_causal_d128", "txl_memory"]
 METRIC = "rel-pos attention fwd TFLOP/s and % of MFMA bf16 peak (1 MI355X)"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0                             # MI355X published HBM3E bandwidth

@@ -124,7 +124,7 @@ typedef enum {
 typedef struct {
     int32_t kind;            /* relattn_kind                                     */
     int32_t dtype;           /* relattn_dtype                                    */
-    int32_t B, H, Lq, Lk, d; /* d in {32, 64}                                    */
+    int32_t B, H, Lq, Lk, d; /* d in {32, 64}, and 128 for BF16                    */
     const void *table;       /* device pointer, see above                        */
     const void *table2;      /* device pointer, see above                        */
     int32_t num_buckets;     /* T5: total buckets (2..256)                       */

@@ -66,6 +66,7 @@ def _fwd_status(lib, p):
 @pytest.mark.parametrize("kw,status", [
     (dict(kind="t5"), 1),                                   # table NULL
     (dict(kind="t5", table=FAKE, d=48), 2),                 # unsupported head dim
+    (dict(kind="t5", dtype="fp32", table=FAKE, d=128), 2),  # 128 is built for bfloat16 only
     (dict(kind="t5", table=FAKE, d=0), 1),
     (dict(kind="t5", table=FAKE, B=0), 1),
     (dict(kind="t5", table=FAKE, Lk=0), 1),

@@ -140,6 +140,19 @@ for dtype in ("fp32", "bf16"):
         ]
 
 
+# 128-wide heads (bfloat16 only)
+SMALL_CASES += [
+    _small("t5", "bf16", 128, valid_len_range=(1, 333)),
+    _small("t5", "bf16", 128, bidirectional=False, causal=True, Lq=200, q_pos_offset=133),
+    _small("shaw", "bf16", 128, clip_k=16, causal=True, Lq=333),
+    _small("shaw", "bf16", 128, clip_k=7, causal=False),
+    _small("deberta", "bf16", 128, clip_k=512),
+    _small("deberta", "bf16", 128, clip_k=16, causal=True, Lq=333, valid_len_range=(50, 333)),
+    _small("alibi", "bf16", 128, causal=True, Lq=333),
+    _small("txl", "bf16", 128, causal=True, Lq=130, q_pos_offset=203, clip_k=333),
+]
+
+
 def _case_id(wl):
     s = f"{wl.kind}-{wl.dtype}-d{wl.d}-Lq{wl.Lq}-Lk{wl.Lk}"
     if wl.kind == "t5":
@@ -278,6 +291,8 @@ DECODE1_CASES = [
              causal=True, q_pos_offset=3999, k_pos_offset=1000),
     Workload(name="dec1", kind="txl", B=2, H=4, Lq=1, Lk=3000, d=64, dtype="bf16",
              causal=True, q_pos_offset=2999, clip_k=3000, table_sigma=0.1),
+    Workload(name="dec1", kind="alibi", B=2, H=4, Lq=1, Lk=2500, d=128, dtype="bf16",
+             causal=True, q_pos_offset=2499),
 ]
 
 

@@ -15,7 +15,7 @@
 namespace relattn {
 hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int grid, int lds,
                       hipStream_t st);
-bool fwd_variant_built(int kind, bool bf, Variant v);
+bool fwd_variant_built(int kind, bool bf, int d, Variant v);
 hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st);
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st);
 hipError_t launch_index(const IndexArgs& a, hipStream_t st);
@@ -118,7 +118,8 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     return fail(RELATTN_ERR_INVALID, "B, H, Lq, Lk must be >= 1 (got %d %d %d %d)",
                 p->B, p->H, p->Lq, p->Lk);
   if (p->d < 1) return fail(RELATTN_ERR_INVALID, "d=%d must be >= 1", p->d);
-  if (p->d != 32 && p->d != 64) return fail(RELATTN_ERR_UNSUPPORTED, "d=%d (built: 32, 64)", p->d);
+  if (p->d != 32 && p->d != 64 && !(p->d == 128 && p->dtype == RELATTN_BF16))
+    return fail(RELATTN_ERR_UNSUPPORTED, "d=%d (built: 32, 64; 128 in bfloat16)", p->d);
   if ((int64_t)p->B * p->H > (1 << 24)) return fail(RELATTN_ERR_UNSUPPORTED, "B*H too large");
   if (p->Lq > (1 << 26) || p->Lk > (1 << 26))
     return fail(RELATTN_ERR_UNSUPPORTED, "sequence length above 2^26");
@@ -179,7 +180,8 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   };
   Variant var = Variant{4, 1};
   int lds_total = 0, lut_n = 0;
-  if ((p->kind == RELATTN_T5 || p->kind == RELATTN_SHAW || p->kind == RELATTN_ALIBI) && P->bf) {
+  if ((p->kind == RELATTN_T5 || p->kind == RELATTN_SHAW || p->kind == RELATTN_ALIBI) && P->bf &&
+      p->d <= 64) {
     const int64_t wgs2 = (int64_t)BH * ((p->Lq + 4 * 64 - 1) / (4 * 64));
     int t2 = 0;
     if (wgs2 >= 2 * kNumCU && lds_for(Variant{4, 2}, &t2, &lut_n) == RELATTN_OK &&
@@ -194,7 +196,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     ls = lds_for(var, &lds_total, &lut_n);
     if (ls != RELATTN_OK) return ls;
   }
-  if (!fwd_variant_built(p->kind, P->bf, var)) return fail(RELATTN_ERR_UNSUPPORTED, "no kernel variant");
+  if (!fwd_variant_built(p->kind, P->bf, p->d, var)) return fail(RELATTN_ERR_UNSUPPORTED, "no kernel variant");
   P->var = var;
   const int BQ = kBlockRows * var.qb * var.nw;
   P->n_qtiles = (p->Lq + BQ - 1) / BQ;

@@ -78,8 +78,8 @@ struct Variant {
 };
 
 // Key/value stages in flight (global -> LDS ring depth) per kind.
-RELATTN_HD constexpr int num_stages(int kind, bool bf16) {
-  return (kind == 0 || kind == 3) ? (bf16 ? 4 : 3) : 2;
+RELATTN_HD constexpr int num_stages(int kind, bool bf16, int d) {
+  return d > 64 ? 2 : ((kind == 0 || kind == 3) ? (bf16 ? 4 : 3) : 2);
 }
 
 // Shaw bins strictly inside the clip window (offsets -k+1 .. k-1), padded to
@@ -124,7 +124,7 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
   const int esz = bf16 ? 2 : 4;
   L.tile_bytes = kBK * d * esz;
   L.stage_bytes = 2 * L.tile_bytes;
-  L.rel_off = num_stages(kind, bf16) * L.stage_bytes;
+  L.rel_off = num_stages(kind, bf16, d) * L.stage_bytes;
   int rel_bytes = 0;
   if (kind == 0) {
     // stride = 16 (mod 64) floats: four lanes reading the four copies at one

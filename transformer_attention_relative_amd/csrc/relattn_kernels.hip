@@ -512,8 +512,12 @@ __device__ __forceinline__ f32x16 mma_keyconst(const KeyConst<BF>& kc, int side,
   }
 }
 
+// Workgroups per CU the register budget is set for: two, except where the
+// LDS of a 128-wide head already allows only one (Shaw, DeBERTa, TXL), which
+// then gets the whole register file.
 template <int KIND, bool BF, int D, int QB, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * NW, (D > 64 && KIND != 0 && KIND != 3) ? 1 : 8 / NW)
+void relattn_fwd_kernel(FwdArgs a) {
   static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
   using T = typename std::conditional<BF, bf16, float>::type;
   using QFrag = TableFrag<BF, D>;
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
   constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
   constexpr int RW = 32 * QB;         // query rows per wave
   constexpr int BQ = RW * NW;         // query rows per workgroup
-  constexpr int NS = num_stages(KIND, BF);
+  constexpr int NS = num_stages(KIND, BF, D);
   using Dma = TileDma<BF, D, NW>;
   constexpr int ROWB = Dma::ROWB;     // bytes per K / V row
   constexpr int LPW = Dma::LPW;       // load instructions per wave per tile
@@ -1218,7 +1222,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void relattn_fwd_kernel(FwdArgs a)
       // One query block per wave leaves registers to spare: the V^T
       // fragments of the step are read before the softmax, so their LDS
       // latency hides behind it instead of sitting between it and P V.
-      constexpr bool EARLY_V = BF && QB == 1;
+      constexpr bool EARLY_V = BF && QB == 1 && D <= 64;
       bf16x8 vpre[EARLY_V ? 2 : 1][EARLY_V ? NDB : 1];
       if constexpr (EARLY_V) {
 #pragma unroll
@@ -1536,7 +1540,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
   return hipGetLastError();
 }
 
-bool fwd_variant_built(int kind, bool bf, Variant v) {
+bool fwd_variant_built(int kind, bool bf, int d, Variant v) {
+  if (d == 128) return bf && v.qb == 1 && v.nw == 4;
   if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
@@ -1550,6 +1555,8 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
   RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
   RA_CASE(K, false, 32, QBV, NWV)
   RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4) RA_DT(4, 1, 4)
+  RA_CASE(0, true, 128, 1, 4) RA_CASE(1, true, 128, 1, 4) RA_CASE(2, true, 128, 1, 4)
+  RA_CASE(3, true, 128, 1, 4) RA_CASE(4, true, 128, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
   RA_CASE(1, true, 64, 2, 4) RA_CASE(1, true, 32, 2, 4)
   RA_CASE(3, true, 64, 2, 4) RA_CASE(3, true, 32, 2, 4)
@@ -1568,7 +1575,8 @@ static void launch_combine_t(const CombineArgs& a, int grid, hipStream_t st) {
 hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) {
   const int64_t threads = (int64_t)a.BH * a.Lq * (d / 4);
   const int grid = (int)((threads + 255) / 256);
-  if (bf && d == 64) launch_combine_t<true, 64>(a, grid, st);
+  if (bf && d == 128) launch_combine_t<true, 128>(a, grid, st);
+  else if (bf && d == 64) launch_combine_t<true, 64>(a, grid, st);
   else if (bf && d == 32) launch_combine_t<true, 32>(a, grid, st);
   else if (!bf && d == 64) launch_combine_t<false, 64>(a, grid, st);
   else launch_combine_t<false, 32>(a, grid, st);
@@ -1578,7 +1586,8 @@ hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) 
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st) {
   const int64_t threads = (int64_t)a.BH * a.Lk;
   const int grid = (int)((threads + 255) / 256);
-  if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
+  if (bf && d == 128) hipLaunchKernelGGL((relattn_colc_kernel<true, 128>), dim3(grid), dim3(256), 0, st, a);
+  else if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
   else if (bf && d == 32) hipLaunchKernelGGL((relattn_colc_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
   else if (!bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((relattn_colc_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);

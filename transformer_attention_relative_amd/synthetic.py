@@ -83,6 +83,11 @@ WORKLOADS = {
         q_pos_offset=3968, causal=True, table_sigma=0.5,
         description="T5 causal decoder with KV cache: 128 queries at positions "
                     "3968..4095 against keys 0..4095, B4 H16 d64 bf16"),
+    "alibi_causal_d128": Workload(
+        name="alibi_causal_d128", kind="alibi", B=4, H=16, Lq=4096, Lk=4096, d=128,
+        dtype="bf16", causal=True,
+        description="ALiBi causal with 128-wide heads, slopes -2^(-8(h+1)/16), "
+                    "B4 H16 L4096 d128 bf16"),
     "txl_memory": Workload(
         name="txl_memory", kind="txl", B=4, H=16, Lq=2048, Lk=4096, d=64, dtype="bf16",
         clip_k=4096, q_pos_offset=2048, causal=True, table_sigma=0.1,
