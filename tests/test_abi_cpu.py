@@ -35,7 +35,7 @@ def test_header_declares_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.relattn_abi_version() == 2
+    assert lib.relattn_abi_version() == ra.binding.ABI_VERSION == 2
 
 
 def _params(**kw):
@@ -162,3 +162,9 @@ def test_host_thresholds_match_exact_criterion(nb, md, bidir):
             base, dist = 0, max(-off, 0)
         got = base + (dist if dist < exact else exact + int((dist >= thr_arr).sum()))
         assert got == t5_bucket_exact(off, bidir, nb, md), (off, got)
+
+
+def test_header_abi_version_matches_binding():
+    src = open(HEADER).read()
+    m = re.search(r"#define RELATTN_ABI_VERSION (\d+)", src)
+    assert m and int(m.group(1)) == ra.binding.ABI_VERSION

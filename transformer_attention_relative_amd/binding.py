@@ -16,6 +16,9 @@ from typing import Optional
 
 from .build import LIB_PATH
 
+# relattn_params layout this binding marshals (RELATTN_ABI_VERSION in the header)
+ABI_VERSION = 2
+
 KINDS = {"t5": 0, "shaw": 1, "deberta": 2, "alibi": 3, "txl": 4}
 DTYPES = {"fp32": 0, "bf16": 1}
 STATUS = {0: "RELATTN_OK", 1: "RELATTN_ERR_INVALID", 2: "RELATTN_ERR_UNSUPPORTED",
@@ -79,6 +82,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.relattn_last_error.restype = ctypes.c_char_p
         lib.relattn_abi_version.argtypes = []
         lib.relattn_abi_version.restype = i32
+        # a library built for another parameter layout would read every
+        # field after the first difference from the wrong offset (pointers
+        # included): refuse it before any call
+        got = lib.relattn_abi_version()
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{p}: ABI version {got}, this binding marshals version "
+                               f"{ABI_VERSION}; rebuild the library")
         if path is None:
             _lib = lib
         return lib
