@@ -104,7 +104,8 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //   SHAW    per wave: arel[rows][2k+2] (input dtype: q.a_K[r] - q.a_K[0]);
 //           per wave: float r2k[rows] (the r = 2k entry, unrounded); per
 //           wave: bin rows [rows][bin_slots] (input dtype), one per query
-//           row of the wave; bf16 only: a_V^T [d][bin_slots]
+//           row of the wave; bf16 only: a_V^T [d][bin_slots]; per wave: a_V
+//           rows 0 and 2k [2][d] (input dtype)
 //   DEBERTA per wave: float band[32][kCbandStride], the content-to-position
 //           band [query][m] and then the position-to-content band [key][n]
 //   TXL     per wave: float band[32][kCbandStride], the position band [query][m]
@@ -114,7 +115,7 @@ constexpr int kCbandStride = 68;  // 64 band columns, padded: rows stay 16-byte 
 struct LdsLayout {
   int stage_bytes, tile_bytes, rel_off, total;
   int lut_stride;
-  int arel_stride, arel_wave_bytes, r2k_off, wscr_off, wscr_wave_bytes, avt_off;
+  int arel_stride, arel_wave_bytes, r2k_off, wscr_off, wscr_wave_bytes, avt_off, avend_off;
   int deb_wave_floats;
 };
 
@@ -141,7 +142,8 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     L.wscr_off = L.r2k_off + nw * rows * 4;
     L.wscr_wave_bytes = rows * shaw_bin_stride(clip_k, esz) * esz;
     L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
-    rel_bytes = L.avt_off + (bf16 ? d * nbin * 2 : 0);
+    L.avend_off = L.avt_off + (bf16 ? d * nbin * 2 : 0);
+    rel_bytes = L.avend_off + nw * 2 * d * esz;  // per wave: a_V rows 0 and 2k
   } else if (kind == 2 || kind == 4) {
     L.deb_wave_floats = kBlockRows * kCbandStride;
     rel_bytes = nw * L.deb_wave_floats * 4;

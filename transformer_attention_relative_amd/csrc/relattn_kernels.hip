@@ -779,6 +779,12 @@ void relattn_fwd_kernel(FwdArgs a) {
         for (int x = 0; x < nbin / 2 / EPV; ++x) zp[x] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
+    // this wave's copy of a_V rows 0 and 2k, read by its epilogue
+    {
+      const T* av = reinterpret_cast<const T*>(a.table2);
+      T* ends = reinterpret_cast<T*>(smem + L.rel_off + L.avend_off) + wave * 2 * D;
+      for (int e = lane; e < 2 * D; e += 64) ends[e] = av[(size_t)(e < D ? 0 : 2 * ck) * D + (e % D)];
+    }
     wave_lds_fence();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = r2k[32 * qb + lq];
@@ -1375,16 +1381,16 @@ void relattn_fwd_kernel(FwdArgs a) {
     if constexpr (KIND == 1) {
       flush_bins(qb);
       // bins 0 and 2k take the row mass not held by the in-window bins
-      const T* av = reinterpret_cast<const T*>(a.table2);
       const float lr_tot = lr_run[qb] + __shfl_xor(lr_run[qb], 32);
       const float w_in = win_run[qb] + __shfl_xor(win_run[qb], 32);
       const float w0 = l_tot - w_in - lr_tot;
+      const T* ends = reinterpret_cast<const T*>(smem + L.rel_off + L.avend_off) + wave * 2 * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int dd = 32 * db + acc_row(i, hh);
-          o[qb][db][i] += w0 * (float)av[dd] + lr_tot * (float)av[(size_t)(2 * ck) * D + dd];
+          o[qb][db][i] += w0 * (float)ends[dd] + lr_tot * (float)ends[D + dd];
         }
     }
     if (qrow[qb] >= a.Lq) continue;
