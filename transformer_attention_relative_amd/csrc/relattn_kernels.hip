@@ -823,6 +823,39 @@ void relattn_fwd_kernel(FwdArgs a) {
                   L.tile_bytes, wave, lane);
   }
 
+  // ---- DeBERTa Kr ring: ring index v = u - ring_c0 of the clip-and-shift
+  // index u = query - key + k (before clamping).  Tile kt reads v in
+  // [-64 kt, 319 - 64 kt]; slot = v mod kRingRows holds Kr[clamp(u)] of this
+  // head, chunk c of slot s at byte s*128 + 16*(c ^ swz_k<8>(s)).
+  constexpr bool KR_RING = deberta_kr_ring(KIND, BF, D, NW);
+  const int ring_c0 = a.q_pos_offset + q0 + ck - 63;
+  char* ring = smem + L.rel_off + L.ring_off;
+  auto ring_slot = [&](const int v) -> int {
+    const int m = v % kRingRows;
+    return m < 0 ? m + kRingRows : m;
+  };
+  // copy the 64 rows v0 .. v0+63 (v0 a multiple of 64): 8 copies of 8 rows,
+  // copy `ins` issued by wave ins % NW
+  auto ring_fill = [&](const int v0, const int ln) {
+    if constexpr (KR_RING) {
+      const T* kr = reinterpret_cast<const T*>(a.table);
+      const int s0 = ring_slot(v0);
+#pragma unroll
+      for (int ins = wave; ins < 8; ins += NW) {
+        const int row = 8 * ins + (ln >> 3), slot = ln & 7;
+        const int u = min(max(ring_c0 + v0 + row, 0), 2 * ck - 1);
+        const int chunk = slot ^ swz_k<8>(row);
+        lds_dma16(kr + ((size_t)u * a.H + h) * D + 8 * chunk, ring + (s0 + 8 * ins) * 128);
+      }
+    }
+  };
+  if constexpr (KR_RING) {
+    if (n_my > 0) {
+#pragma unroll
+      for (int g = 0; g < 5; ++g) ring_fill(-64 * kt_begin + 64 * g, lane);
+    }
+  }
+
   // ---- running state ------------------------------------------------------
   // m_ref: the row's reference max in log2 units (both lane halves agree);
   // -inf until the row has seen a visible key.  p = exp2(s - m_ref) is used
@@ -944,6 +977,10 @@ void relattn_fwd_kernel(FwdArgs a) {
       dma.init(wave, opaque_lane());
       dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
                 smem + ((r + NS - 1) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
+    }
+    // the next tile's 64 new Kr rows (they replace rows no tile reads again)
+    if constexpr (KR_RING) {
+      if (r + 1 < n_my) ring_fill(-64 * (kt + 1), lane);
     }
     if constexpr (CLS == 3) return;
     const char* ktile = smem + (r % NS) * L.stage_bytes;
@@ -1124,8 +1161,14 @@ void relattn_fwd_kernel(FwdArgs a) {
             // together, so their L2 latencies overlap instead of adding up
             TableFrag<BF, D> af[2], bfr[2];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-              af[tb].load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
+            for (int tb = 0; tb < 2; ++tb) {
+              if constexpr (KR_RING) {
+                // rows u = T0 + 32 tb + lane + k: 32 consecutive ring slots
+                af[tb].load_lds(ring + ring_slot(T0 + 32 * tb + ck - ring_c0) * 128, ko.k);
+              } else {
+                af[tb].load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
+              }
+            }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
               bfr[nb].load(qr + ((size_t)deberta_delta_dev(-(T0 + 32 * nb + lq), ck) * a.H + h) * D, hh);
@@ -1548,6 +1591,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 
 bool fwd_variant_built(int kind, bool bf, int d, Variant v) {
   if (d == 128) return bf && v.qb == 1 && v.nw == 4;
+  if (kind == 2 && bf && d == 64) return v.qb == 1 && v.nw == 8;
   if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
@@ -1561,6 +1605,7 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
   RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
   RA_CASE(K, false, 32, QBV, NWV)
   RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4) RA_DT(4, 1, 4)
+  RA_CASE(2, true, 64, 1, 8)
   RA_CASE(0, true, 128, 1, 4) RA_CASE(1, true, 128, 1, 4) RA_CASE(2, true, 128, 1, 4)
   RA_CASE(3, true, 128, 1, 4) RA_CASE(4, true, 128, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
