@@ -179,8 +179,10 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     return RELATTN_OK;
   };
   Variant var = Variant{4, 1};
-  // DeBERTa bf16, d = 64: eight waves share one ring of Kr rows in LDS
-  if (p->kind == RELATTN_DEBERTA && P->bf && p->d == 64) var = Variant{8, 1};
+  // DeBERTa / Transformer-XL bf16, d = 64: eight waves share one ring of
+  // band rows in LDS
+  if ((p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) && P->bf && p->d == 64)
+    var = Variant{8, 1};
   int lds_total = 0, lut_n = 0;
   if ((p->kind == RELATTN_T5 || p->kind == RELATTN_SHAW || p->kind == RELATTN_ALIBI) && P->bf &&
       p->d <= 64) {

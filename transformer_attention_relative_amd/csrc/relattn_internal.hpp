@@ -110,7 +110,8 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //           band [query][m] and then the position-to-content band [key][n];
 //           bf16, d = 64, 8 waves: the Kr ring [kRingRows][d] (rows
 //           XOR-swizzled like the K tiles)
-//   TXL     per wave: float band[32][kCbandStride], the position band [query][m]
+//   TXL     per wave: float band[32][kCbandStride], the position band
+//           [query][m]; bf16, d = 64, 8 waves: the E ring, as DeBERTa's
 constexpr int kCbandStride = 68;  // 64 band columns, padded: rows stay 16-byte aligned and
                                   // a query's diagonal (stride 69) hits distinct banks
 
@@ -119,16 +120,17 @@ struct LdsLayout {
   int lut_stride;
   int arel_stride, arel_wave_bytes, r2k_off, wscr_off, wscr_wave_bytes, avt_off, avend_off;
   int deb_wave_floats;
-  int ring_off;  // DeBERTa bf16, d = 64, 8 waves: ring of Kr rows (kRingRows x 128 B)
+  int ring_off;  // DeBERTa / TXL bf16, d = 64, 8 waves: ring of band rows (kRingRows x 128 B)
 };
 
-// DeBERTa's content-to-position rows of a workgroup of 8 waves x 32 query
-// rows: a tile of 64 keys reads 320 consecutive Kr rows, the next tile 64
-// rows below them, so a ring of 384 rows holds one tile's rows and the
-// next tile's new ones.
+// The band rows of a workgroup of 8 waves x 32 query rows (DeBERTa's Kr
+// rows of the content-to-position band, Transformer-XL's encodings E): a
+// tile of 64 keys reads 320 consecutive rows, the next tile 64 rows below
+// them, so a ring of 384 rows holds one tile's rows and the next tile's new
+// ones.
 constexpr int kRingRows = 384;
-RELATTN_HD constexpr bool deberta_kr_ring(int kind, bool bf16, int d, int nw) {
-  return kind == 2 && bf16 && d == 64 && nw == 8;
+RELATTN_HD constexpr bool band_ring(int kind, bool bf16, int d, int nw) {
+  return (kind == 2 || kind == 4) && bf16 && d == 64 && nw == 8;
 }
 
 RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int nw, int clip_k,
@@ -159,7 +161,7 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
   } else if (kind == 2 || kind == 4) {
     L.deb_wave_floats = kBlockRows * kCbandStride;
     rel_bytes = nw * L.deb_wave_floats * 4;
-    if (deberta_kr_ring(kind, bf16, d, nw)) {
+    if (band_ring(kind, bf16, d, nw)) {
       L.ring_off = rel_bytes;
       rel_bytes += kRingRows * d * 2;
     }

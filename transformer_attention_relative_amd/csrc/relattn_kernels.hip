@@ -823,12 +823,16 @@ void relattn_fwd_kernel(FwdArgs a) {
                   L.tile_bytes, wave, lane);
   }
 
-  // ---- DeBERTa Kr ring: ring index v = u - ring_c0 of the clip-and-shift
-  // index u = query - key + k (before clamping).  Tile kt reads v in
-  // [-64 kt, 319 - 64 kt]; slot = v mod kRingRows holds Kr[clamp(u)] of this
-  // head, chunk c of slot s at byte s*128 + 16*(c ^ swz_k<8>(s)).
-  constexpr bool KR_RING = deberta_kr_ring(KIND, BF, D, NW);
-  const int ring_c0 = a.q_pos_offset + q0 + ck - 63;
+  // ---- band-row ring (DeBERTa Kr, Transformer-XL E): ring index
+  // v = u - ring_c0 of the row index before clamping, u = query - key + k
+  // (DeBERTa's clip-and-shift) or u = query - key (TXL's distance).  Tile kt
+  // reads v in [-64 kt, 319 - 64 kt]; slot = v mod kRingRows holds the
+  // clamped row of this head, chunk c of slot s at byte s*128 +
+  // 16*(c ^ swz_k<8>(s)).
+  constexpr bool KR_RING = band_ring(KIND, BF, D, NW);
+  const int ring_k = KIND == 2 ? ck : 0;                     // u - (query - key)
+  const int ring_rows = KIND == 2 ? 2 * ck : ck;             // rows of the table
+  const int ring_c0 = a.q_pos_offset + q0 + ring_k - 63;
   char* ring = smem + L.rel_off + L.ring_off;
   auto ring_slot = [&](const int v) -> int {
     const int m = v % kRingRows;
@@ -843,7 +847,7 @@ void relattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int ins = wave; ins < 8; ins += NW) {
         const int row = 8 * ins + (ln >> 3), slot = ln & 7;
-        const int u = min(max(ring_c0 + v0 + row, 0), 2 * ck - 1);
+        const int u = min(max(ring_c0 + v0 + row, 0), ring_rows - 1);
         const int chunk = slot ^ swz_k<8>(row);
         lds_dma16(kr + ((size_t)u * a.H + h) * D + 8 * chunk, ring + (s0 + 8 * ins) * 128);
       }
@@ -1123,8 +1127,13 @@ void relattn_fwd_kernel(FwdArgs a) {
           const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
           TableFrag<BF, D> ef[2];
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)  // negative distances are hidden keys: any row serves
-            ef[tb].load(enc + ((size_t)min(max(T0 + 32 * tb + lq, 0), ck - 1) * a.H + h) * D, hh);
+          for (int tb = 0; tb < 2; ++tb) {  // negative distances are hidden keys: any row serves
+            if constexpr (KR_RING) {
+              ef[tb].load_lds(ring + ring_slot(T0 + 32 * tb - ring_c0) * 128, ko.k);
+            } else {
+              ef[tb].load(enc + ((size_t)min(max(T0 + 32 * tb + lq, 0), ck - 1) * a.H + h) * D, hh);
+            }
+          }
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             const f32x16 acc = mma_frag0<BF, D>(ef[tb], qv[qb]);
@@ -1591,7 +1600,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 
 bool fwd_variant_built(int kind, bool bf, int d, Variant v) {
   if (d == 128) return bf && v.qb == 1 && v.nw == 4;
-  if (kind == 2 && bf && d == 64) return v.qb == 1 && v.nw == 8;
+  if ((kind == 2 || kind == 4) && bf && d == 64) return v.qb == 1 && v.nw == 8;
   if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
@@ -1605,7 +1614,7 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
   RA_CASE(K, true, 64, QBV, NWV) RA_CASE(K, true, 32, QBV, NWV) RA_CASE(K, false, 64, QBV, NWV) \
   RA_CASE(K, false, 32, QBV, NWV)
   RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4) RA_DT(4, 1, 4)
-  RA_CASE(2, true, 64, 1, 8)
+  RA_CASE(2, true, 64, 1, 8) RA_CASE(4, true, 64, 1, 8)
   RA_CASE(0, true, 128, 1, 4) RA_CASE(1, true, 128, 1, 4) RA_CASE(2, true, 128, 1, 4)
   RA_CASE(3, true, 128, 1, 4) RA_CASE(4, true, 128, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
