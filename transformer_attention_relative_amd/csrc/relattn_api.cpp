@@ -180,8 +180,10 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   };
   Variant var = Variant{4, 1};
   // DeBERTa / Transformer-XL bf16, d = 64: eight waves share one ring of
-  // band rows in LDS
-  if ((p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) && P->bf && p->d == 64)
+  // band rows in LDS (DeBERTa with a narrow clip window has few band blocks
+  // and keeps two four-wave workgroups per CU)
+  if (((p->kind == RELATTN_DEBERTA && p->clip_k >= 64) || p->kind == RELATTN_TXL) && P->bf &&
+      p->d == 64)
     var = Variant{8, 1};
   int lds_total = 0, lut_n = 0;
   if ((p->kind == RELATTN_T5 || p->kind == RELATTN_SHAW || p->kind == RELATTN_ALIBI) && P->bf &&

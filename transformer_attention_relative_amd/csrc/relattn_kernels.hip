@@ -1600,7 +1600,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 
 bool fwd_variant_built(int kind, bool bf, int d, Variant v) {
   if (d == 128) return bf && v.qb == 1 && v.nw == 4;
-  if ((kind == 2 || kind == 4) && bf && d == 64) return v.qb == 1 && v.nw == 8;
+  if ((kind == 2 || kind == 4) && bf && d == 64) return v.qb == 1 && (v.nw == 8 || v.nw == 4);
   if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
 }
