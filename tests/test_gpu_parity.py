@@ -140,6 +140,20 @@ for dtype in ("fp32", "bf16"):
         ]
 
 
+# the shared LDS ring of band rows (bfloat16, d = 64: DeBERTa with a clip
+# window of 64 or more, Transformer-XL): workgroups of 256 query rows, a
+# ragged last workgroup, causal masks, padding, shifted key positions
+SMALL_CASES += [
+    _small("deberta", "bf16", 64, clip_k=64, causal=True, Lq=333, valid_len_range=(40, 333)),
+    _small("deberta", "bf16", 64, clip_k=100, Lq=300, Lk=700, q_pos_offset=150,
+           valid_len_range=(300, 700)),
+    _small("deberta", "bf16", 64, clip_k=700, causal=True, Lq=520, Lk=900, q_pos_offset=380),
+    _small("txl", "bf16", 64, causal=True, Lq=300, Lk=800, q_pos_offset=500, clip_k=800,
+           valid_len_range=(600, 800)),
+    _small("txl", "bf16", 64, causal=True, Lq=257, Lk=500, q_pos_offset=700, k_pos_offset=457,
+           clip_k=600),
+]
+
 # 128-wide heads (bfloat16 only)
 SMALL_CASES += [
     _small("t5", "bf16", 128, valid_len_range=(1, 333)),
