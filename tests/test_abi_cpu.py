@@ -131,6 +131,24 @@ def test_workspace_sizes():
                 causal=1, bidirectional=0)
     n = ra.relattn_workspace_bytes(p)
     assert n >= 2 * 64 * 128 * (64 + 2) * 4 and n % 256 == 0
+    # ALiBi and Transformer-XL need no per-key pass; a one-token decode step
+    # splits its key range
+    p = _params(kind="alibi", table=FAKE, B=4, H=16, Lq=4096, Lk=4096, causal=1)
+    assert ra.relattn_workspace_bytes(p) == 0
+    p = _params(kind="txl", table=FAKE, table2=FAKE, clip_k=4096, B=4, H=16, Lq=2048,
+                Lk=4096, q_pos_offset=2048, causal=1)
+    assert ra.relattn_workspace_bytes(p) == 0
+    p = _params(kind="alibi", table=FAKE, B=4, H=16, Lq=1, Lk=3072, q_pos_offset=4095,
+                k_pos_offset=1024, causal=1)
+    n = ra.relattn_workspace_bytes(p)
+    assert n >= 2 * 64 * 1 * (64 + 2) * 4 and n % 256 == 0
+    # 128-wide heads in bfloat16 (enough workgroups: no split)
+    p = _params(kind="shaw", table=FAKE, table2=FAKE, clip_k=16, d=128, B=4, H=16, Lq=2048,
+                Lk=2048, causal=1)
+    assert ra.relattn_workspace_bytes(p) == 0
+    p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=64, d=128, B=4, H=16, Lq=2048,
+                Lk=2048)
+    assert ra.relattn_workspace_bytes(p) == 64 * 2048 * 8
 
 
 def test_rel_index_validation(lib):
