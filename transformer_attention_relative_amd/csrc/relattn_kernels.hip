@@ -630,8 +630,10 @@ void relattn_fwd_kernel(FwdArgs a) {
   float bias_left = 0.f, bias_right = 0.f;          // T5 saturated buckets / scale
   constexpr int SHAW_RB = 3;                          // blocks of 32 a_K rows (k <= 32)
   TableFrag<BF, D> krow[KIND == 1 ? SHAW_RB : 1];     // Shaw a_K rows / DeBERTa Kr rows
-  constexpr int AVT_EARLY = 8;
-  T avt_early[AVT_EARLY];
+  // Shaw bf16: a_V rows 1 .. 2k-1 in 16-byte chunks, read row-major
+  // (coalesced) here and written transposed into LDS by the prologue
+  constexpr int AVT_CH = (63 * (D / 8) + 64 * NW - 1) / (64 * NW);
+  bf16x8 avt_ch[KIND == 1 && BF ? AVT_CH : 1];
   if constexpr (KIND == 0) {
     const float* tab = reinterpret_cast<const float*>(a.table);
 #pragma unroll
@@ -655,16 +657,13 @@ void relattn_fwd_kernel(FwdArgs a) {
     for (int rb = 0; rb < SHAW_RB; ++rb)
       if (rb * 32 < nrow) krow[rb].load(ak + (size_t)min(rb * 32 + lq, nrow - 1) * D, hh);
     if constexpr (BF) {
-      const int nb = shaw_bin_slots(ck);
-      const T* av = reinterpret_cast<const T*>(a.table2);
+      const bf16* av = reinterpret_cast<const bf16*>(a.table2);
+      const int nch = (2 * ck - 1) * (D / 8);
 #pragma unroll
-      for (int i = 0; i < AVT_EARLY; ++i) {
-        const int e = tid + i * 64 * NW;
-        avt_early[i] = (T)0.f;
-        if (e < D * nb) {
-          const int dd = e / nb, r = e - dd * nb;
-          if (r < 2 * ck - 1) avt_early[i] = av[(size_t)(r + 1) * D + dd];
-        }
+      for (int c = 0; c < AVT_CH; ++c) {
+        const int e = tid + c * 64 * NW;
+        avt_ch[c] = bf16x8{};
+        if (e < nch) avt_ch[c] = *reinterpret_cast<const bf16x8*>(av + (size_t)(e / (D / 8) + 1) * D + 8 * (e % (D / 8)));
       }
     }
   } else if constexpr (KIND == 2) {
@@ -792,16 +791,19 @@ void relattn_fwd_kernel(FwdArgs a) {
       // a_V^T for the in-window bins: avt[d][r'] = a_V[r' + 1][d], r' < 2k - 1
       const int nb = shaw_bin_slots(ck);
       T* avt = reinterpret_cast<T*>(smem + L.rel_off + L.avt_off);
-      const T* av = reinterpret_cast<const T*>(a.table2);
+      const int nch = (2 * ck - 1) * (D / 8);
 #pragma unroll
-      for (int i = 0; i < AVT_EARLY; ++i) {
-        const int e = tid + i * 64 * NW;
-        if (e < D * nb) avt[e] = avt_early[i];
+      for (int c = 0; c < AVT_CH; ++c) {
+        const int e = tid + c * 64 * NW;
+        if (e < nch) {
+          const int r = e / (D / 8), d0 = 8 * (e % (D / 8));
+#pragma unroll
+          for (int q = 0; q < 8; ++q) avt[(d0 + q) * nb + r] = avt_ch[c][q];
+        }
       }
-      for (int e = tid + AVT_EARLY * 64 * NW; e < D * nb; e += 64 * NW) {
-        const int dd = e / nb, r = e - dd * nb;
-        avt[e] = r < 2 * ck - 1 ? av[(size_t)(r + 1) * D + dd] : (T)0.f;
-      }
+      // the padding bins 2k-1 .. nb-1 meet zero rows
+      const int npad = nb - (2 * ck - 1);
+      for (int e = tid; e < D * npad; e += 64 * NW) avt[(e / npad) * nb + 2 * ck - 1 + e % npad] = (T)0.f;
     }
   } else if constexpr (KIND == 2) {
 #pragma unroll
