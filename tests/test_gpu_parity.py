@@ -422,6 +422,47 @@ def test_lse_of_rows_without_keys_is_minus_inf():
 
 
 # ----------------------------------------------------------------------------
+# 2d. a seeded sweep of random small configurations across every feature
+# ----------------------------------------------------------------------------
+
+def _random_case(i):
+    rng = np.random.default_rng(1000 + i)
+    kind = ["t5", "shaw", "deberta", "alibi", "txl"][i % 5]
+    dtype, d = [("bf16", 64), ("bf16", 32), ("fp32", 64), ("fp32", 32), ("bf16", 128)][(i // 5) % 5]
+    Lq = int(rng.choice([1, 2, 31, 33, 64, 97, 130, 257]))
+    Lk = int(rng.choice([1, 5, 63, 64, 65, 200, 333, 700]))
+    causal = bool(rng.integers(2)) or kind == "txl"
+    qpo = int(rng.integers(0, 600))
+    kpo = int(rng.integers(0, 600))
+    kw = dict(name="rnd", kind=kind, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), Lq=Lq,
+              Lk=Lk, d=d, dtype=dtype, causal=causal, q_pos_offset=qpo, k_pos_offset=kpo,
+              table_sigma=0.5 if kind == "t5" else 0.1)
+    if rng.integers(3) == 0:
+        kw["valid_len_range"] = (0, Lk)
+    if kind == "t5":
+        kw.update(num_buckets=int(rng.choice([8, 16, 32, 64])), bidirectional=not causal)
+        kw["max_distance"] = int(rng.choice([kw["num_buckets"], 128, 1000]))
+    elif kind == "shaw":
+        kw["clip_k"] = int(rng.choice([1, 4, 16, 32]))
+    elif kind == "deberta":
+        kw["clip_k"] = int(rng.choice([1, 8, 64, 512]))
+    elif kind == "txl":
+        kw["clip_k"] = max(1, qpo + Lq - kpo) + int(rng.integers(0, 50))
+    return Workload(**kw)
+
+
+RANDOM_CASES = [_random_case(i) for i in range(50)]
+
+
+@pytest.mark.parametrize("wl", RANDOM_CASES, ids=lambda w: _case_id(w) + f"-B{w.B}H{w.H}")
+def test_parity_random_configurations(wl):
+    inp = make_inputs(wl, seed=21)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    check_close(got, want, wl.dtype, _case_id(wl))
+
+
+# ----------------------------------------------------------------------------
 # 3. the five workloads at full size, in the benchmark's launch configuration;
 #    the oracle computes sampled (batch, head) pairs and query rows
 # ----------------------------------------------------------------------------
