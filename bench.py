@@ -284,6 +284,20 @@ def calibrate_copy(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
+def measured_mfma_peak():
+    """Sustained v_mfma_f32_32x32x16_bf16 rate (TFLOP/s) from the probe library
+    built beside librelattn.so, or None if it is not there."""
+    import ctypes
+    path = os.path.join(ROOT, "transformer_attention_relative_amd", "libmfma_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mfma_peak_bf16_tflops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mfma_peak_bf16_tflops.restype = ctypes.c_double
+    best = max(lib.mfma_peak_bf16_tflops(512, 20000) for _ in range(3))
+    return round(best, 1) if best > 0 else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +349,10 @@ def main():
                    "host_wall_ms_per_step": round(wall_ms, 5)},
         "roofline": roofline(wl, flops, nbytes, ms, read_traffic(wl.name)),
     }
+    probe = measured_mfma_peak() if wl.dtype == "bf16" else None
+    if probe:
+        rec["config"]["mfma_measured_peak_tflops"] = probe
+        rec["config"]["mfma_measured_peak_frac"] = round(tflops / probe, 4)
     if not args.no_secondary:
         sec = {}
         for name in SECONDARY:
@@ -345,6 +363,8 @@ def main():
             sec[name] = {"tflops": round(t2, 2), "ms_per_step": round(ms2, 5),
                          "mfma_peak_frac": round(t2 / PEAK_TFLOPS[w2.dtype], 4),
                          "roofline": roofline(w2, f2, b2, ms2, read_traffic(name))}
+            if probe and w2.dtype == "bf16":
+                sec[name]["mfma_measured_peak_frac"] = round(t2 / probe, 4)
         rec["secondary"] = sec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp)

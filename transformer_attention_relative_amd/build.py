@@ -20,6 +20,9 @@ LIB_NAME = "librelattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["relattn_kernels.hip", "relattn_api.cpp"]
+# the benchmark's MFMA peak probe, a separate library
+PROBE_SOURCE = "mfma_peak.hip"
+PROBE_PATH = os.path.join(PKG_DIR, "libmfma_peak.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,17 +46,24 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librelattn.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source of the library for gfx950; return the .so path."""
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out_path):
+    tmp = out_path + ".tmp"
     cmd = [hipcc_path(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    t0 = time.time()
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
         raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd)}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
+    return proc
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source for gfx950 (the library and the benchmark's
+    MFMA probe); return the library's .so path."""
+    t0 = time.time()
+    proc = _compile(SOURCES, LIB_PATH)
+    _compile([PROBE_SOURCE], PROBE_PATH)
     if verbose:
         noisy = [l for l in (proc.stdout + proc.stderr).splitlines()
                  if "packed-fp32-ops" not in l]
