@@ -977,13 +977,24 @@ void relattn_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     const int k0 = kt * kBK;
-    if (r + NS - 1 < n_my) {
-      // copy offsets from a fresh lane id: kept out of registers between tiles
-      Dma dma;
-      dma.init(wave, opaque_lane());
-      dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
-                smem + ((r + NS - 1) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
-    }
+    // Lean tiles in bfloat16 run as a software pipeline (below); T5 with two
+    // query blocks per wave or 128-wide heads keeps the step loop (the
+    // pipeline's extra live registers spill there)
+    constexpr bool PIPE = CLS != 2 && CLS != 3 && BF && KIND != 4 && !(KIND == 0 && (QB == 2 || D > 64));
+    // copies of the tile NS - 1 ahead into the stage of tile r - 1 (free:
+    // every wave has passed the barrier above)
+    auto issue_next = [&]() {
+      if (r + NS - 1 < n_my) {
+        // copy offsets from a fresh lane id: kept out of registers between tiles
+        Dma dma;
+        dma.init(wave, opaque_lane());
+        dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
+                  smem + ((r + NS - 1) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
+      }
+    };
+    // a pipelined tile issues them after its first scores, so that its
+    // first MFMAs do not wait for the copies' address arithmetic
+    if constexpr (!PIPE) issue_next();
     // the next tile's 64 new Kr rows (they replace rows no tile reads again)
     if constexpr (KR_RING) {
       if (r + 1 < n_my) ring_fill(-64 * (kt + 1), lane);
@@ -1392,7 +1403,129 @@ void relattn_fwd_kernel(FwdArgs a) {
       }
     };
 
-    if constexpr (CLS != 2) {
+    // Lean tiles (classes 0 and 1) in bfloat16: a software pipeline over
+    // the tile's NKB*QB blocks of 32 keys x 32 query rows (block g: key
+    // block g / QB, query block g % QB).  The code of block g holds the
+    // scores of block g+1 and the P V product of block g-1 beside block g's
+    // exponentials: none depends on the others, so the MFMAs run while the
+    // vector ALU computes the softmax, within one wave.
+    auto pipe_tile = [&]() {
+      constexpr int NB = NKB * QB;
+      // raw scores of block g: the in-block relative term + q.k
+      auto block_scores = [&](const int g, const TableFrag<BF, D>& kf) -> f32x16 {
+        const int kb = g / QB, qb = g % QB;
+        if constexpr (KIND == 0) {
+          if constexpr (CLS == 1) {
+            f32x16 init;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(lutp[qb] + 32 * kb + 8 * q4 + 4 * hh);
+              init[4 * q4 + 0] = x[0]; init[4 * q4 + 1] = x[1];
+              init[4 * q4 + 2] = x[2]; init[4 * q4 + 3] = x[3];
+            }
+            return mma_frag<BF, D>(kf, qf[qb], init);
+          } else {
+            return mma_frag0<BF, D>(kf, qf[qb]);
+          }
+        } else if constexpr (KIND == 2) {
+          return mma_frag<BF, D>(kf, qf[qb], mma_keyconst<BF>(kc[kb], deb_side[qb], hh));
+        } else if constexpr (KIND == 3) {
+          return mma_frag<BF, D>(kf, qf[qb], mma_keyconst<BF>(alibi_kc, deb_side[qb], hh));
+        } else {
+          return mma_frag0<BF, D>(kf, qf[qb]);
+        }
+      };
+      // per-row constant of block g (raw score units)
+      auto block_b = [&](const int g) -> float {
+        const int kb = g / QB, qb = g % QB;
+        if constexpr (KIND == 3) {
+          const float dist = (float)(pos[qb] - (k0 + 32 * kb));
+          return deb_side[qb] == 0 ? alibi_s * dist : -alibi_s * dist;
+        }
+        return b_tile[qb];
+      };
+      auto block_off = [&](const int g) -> float {
+        if constexpr (KIND == 3) return ref_offset(c * block_b(g), m_ref[g % QB]);
+        return off[g % QB];
+      };
+      // p = exp2(mul * x + add) in place, its bfloat16 copy, the lane sum
+      auto smax = [&](f32x16& x, bf16x8 (&pb)[2], const float mul, const float add) -> float {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = fast_exp2(fmaf(x[i], mul, add));
+        float ls = 0.f;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          pb[h2] = pack_bf16x8(x, 8 * h2);
+          ls = sum_bf16x8(pb[h2], ls);
+        }
+        return ls;
+      };
+      f32x16 sc[2];
+      bf16x8 pb[2][2];
+      bf16x8 vf[2][NDB];  // V^T fragments of the key block of the pending P V
+      auto load_v = [&](const int kb) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) vf[h2][db] = load_vt_frag<D>(vtile, 2 * kb + h2, ko.v[db]);
+      };
+      auto pv = [&](const int g) {
+        const int qb = g % QB;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[qb][db] = mma_bf16(vf[h2][db], pb[g & 1][h2], o[qb][db]);
+      };
+      {
+        TableFrag<BF, D> kf;
+        kf.load_lds(ktile, ko.k);
+        sc[0] = block_scores(0, kf);
+      }
+      issue_next();
+#pragma unroll
+      for (int g = 0; g < NB; ++g) {
+        const int kb = g / QB, qb = g % QB;
+        if (g >= 1 && (g - 1) % QB == 0) load_v((g - 1) / QB);
+        if (g + 1 < NB) {
+          TableFrag<BF, D> kf;
+          kf.load_lds(ktile + 32 * ((g + 1) / QB) * ROWB, ko.k);
+          sc[(g + 1) & 1] = block_scores(g + 1, kf);
+        }
+        float ls = smax(sc[g & 1], pb[g & 1], c, block_off(g));
+        if (g >= 1) pv(g - 1);
+        if (__builtin_expect(__any(ls > kSumLimit), 0)) {
+          // exact path: the block's scores in log2 units, the row max, the
+          // rescale of the running state, the softmax again
+          TableFrag<BF, D> kf2;
+          kf2.load_lds(ktile + 32 * kb * ROWB, ko.k);
+          f32x16 x = block_scores(g, kf2);
+          const float cb = c * block_b(g);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = fmaf(x[i], c, cb);
+          const float mn = fmaxf(m_ref[qb], max_halves(max16(x)));
+          const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m_ref[qb] - mn);
+          if constexpr (KIND == 1) flush_bins(qb);  // bins hold p at the old reference
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[qb][db] *= alpha;
+          l_run[qb] *= alpha;
+          lr_run[qb] *= alpha;
+          win_run[qb] *= alpha;
+          m_ref[qb] = mn;
+          ls = smax(x, pb[g & 1], 1.f, -(mn == NEG_INF ? 0.f : mn));
+          off[qb] = ref_offset(c * b_tile[qb], m_ref[qb]);
+        }
+        l_run[qb] += ls;
+        if constexpr (KIND == 1) {
+          if (far_right[qb]) lr_run[qb] += ls;
+        }
+      }
+      if constexpr (QB == 1) load_v(NKB - 1);
+      pv(NB - 1);
+    };
+
+    if constexpr (PIPE) {
+      pipe_tile();
+    } else if constexpr (CLS != 2) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) step(std::integral_constant<int, (1 << QB) - 1>{}, kb);
     } else {
