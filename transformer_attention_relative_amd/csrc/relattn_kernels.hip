@@ -985,9 +985,12 @@ void relattn_fwd_kernel(FwdArgs a) {
     // every wave has passed the barrier above)
     auto issue_next = [&]() {
       if (r + NS - 1 < n_my) {
-        // copy offsets from a fresh lane id: kept out of registers between tiles
+        // copy offsets: kept in registers across tiles with one query block
+        // per wave; recomputed from a fresh lane id where registers are
+        // short (two query blocks, DeBERTa's four-wave variant)
+        constexpr bool KEEP = QB == 1 && !(KIND == 2 && NW == 4);
         Dma dma;
-        dma.init(wave, opaque_lane());
+        dma.init(wave, KEEP ? lane : opaque_lane());
         dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
                   smem + ((r + NS - 1) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
       }
