@@ -599,6 +599,13 @@ RAMP_CASES = [
     _small("shaw", "bf16", 64, clip_k=8, Lq=260, Lk=700),
     _small("deberta", "fp32", 64, clip_k=64, Lq=200, Lk=700),
     _small("deberta", "bf16", 64, clip_k=100, causal=True, Lq=700, Lk=700),
+    _small("alibi", "bf16", 64, Lq=260, Lk=700),
+    _small("alibi", "bf16", 64, causal=True, Lq=700, Lk=700),
+    # B*H = 512 heads of 256 rows: the launcher gives each wave two query
+    # blocks (the benchmark's layout for T5, Shaw and ALiBi at long lengths)
+    _small("t5", "bf16", 64, B=2, H=256, Lq=256, Lk=600),
+    _small("shaw", "bf16", 64, clip_k=8, B=2, H=256, Lq=256, Lk=600),
+    _small("alibi", "bf16", 64, causal=True, B=2, H=256, Lq=256, Lk=256, q_pos_offset=344),
 ]
 
 
@@ -621,12 +628,16 @@ def test_reference_moves_with_growing_scores(wl):
     assert err.mean() <= STRESS_TOL[wl.dtype][1], err.mean()
 
 
-@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta"])
-def test_late_score_jump_is_exact(kind):
+@pytest.mark.parametrize("kind,two_blocks", [("t5", False), ("shaw", False), ("deberta", False),
+                                             ("alibi", False), ("t5", True), ("shaw", True),
+                                             ("alibi", True)])
+def test_late_score_jump_is_exact(kind, two_blocks):
     # the last 40 keys score ~10x higher than the rest: their exponentials
     # overflow the running reference (exp2 of hundreds), which the kernel must
     # detect and redo exactly
-    wl = _small(kind, "bf16", 64, Lq=130, Lk=600, clip_k=16 if kind != "t5" else 0)
+    wl = _small(kind, "bf16", 64, Lq=130, Lk=600, clip_k=16 if kind in ("shaw", "deberta") else 0)
+    if two_blocks:
+        wl = wl.replace(B=2, H=256, Lq=256)
     inp = make_inputs(wl, seed=22)
     k = inp["k"].float()
     k[:, :, -40:] *= 12.0
