@@ -987,8 +987,9 @@ void relattn_fwd_kernel(FwdArgs a) {
       if (r + NS - 1 < n_my) {
         // copy offsets: kept in registers across tiles with one query block
         // per wave; recomputed from a fresh lane id where registers are
-        // short (two query blocks, DeBERTa's four-wave variant)
-        constexpr bool KEEP = QB == 1 && !(KIND == 2 && NW == 4);
+        // short (two query blocks, 128-wide heads, DeBERTa's four-wave
+        // variant)
+        constexpr bool KEEP = QB == 1 && D <= 64 && !(KIND == 2 && NW == 4);
         Dma dma;
         dma.init(wave, KEEP ? lane : opaque_lane());
         dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
