@@ -487,6 +487,29 @@ def test_parity_full_size_sampled(name):
     assert np.isfinite(got).all()
 
 
+# Per-sequence valid lengths without a causal mask: the kernel orders its
+# work by sequence length and rearranges dispatch positions (384 and 400
+# workgroups here: 48 and 50 per XCD, two per CU), so every head and every
+# row is compared, not a sample.
+ORDERED_CASES = [
+    WORKLOADS["t5_encoder_padded"],
+    Workload(name="ord", kind="t5", B=5, H=20, Lq=512, Lk=400, d=64, dtype="bf16",
+             valid_len_range=(1, 400)),
+    Workload(name="ord", kind="alibi", B=6, H=16, Lq=512, Lk=333, d=64, dtype="bf16",
+             valid_len_range=(0, 333), table_sigma=0.1),
+    Workload(name="ord", kind="shaw", B=3, H=10, Lq=256, Lk=300, d=64, dtype="bf16",
+             clip_k=16, valid_len_range=(40, 300), table_sigma=0.1),
+]
+
+
+@pytest.mark.parametrize("wl", ORDERED_CASES, ids=lambda w: _case_id(w) + f"-B{w.B}H{w.H}")
+def test_parity_every_head_with_valid_lengths(wl):
+    inp = make_inputs(wl, seed=3)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    check_close(got, want, wl.dtype, _case_id(wl))
+
+
 # ----------------------------------------------------------------------------
 # 4. properties: determinism, masking independence, empty rows, readouts
 # ----------------------------------------------------------------------------

@@ -102,7 +102,7 @@ struct Plan {
   bool bf;
   float scale;
   Variant var;
-  int n_qtiles, n_splits, grid, lds;
+  int n_qtiles, n_splits, grid, lds, cu_slots;
   size_t off_part_o, off_part_ml, off_colc, ws_bytes;
   T5Plan t5;
 };
@@ -228,6 +228,14 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   P->grid = (int)grid;
   if (lds_total > kLdsPerCU) return fail(RELATTN_ERR_UNSUPPORTED, "LDS need %d B above 160 KiB", lds_total);
   P->lds = lds_total;
+  // workgroups a CU holds at once: LDS, and the register budget the kernels
+  // are built for (two workgroups, one for 128-wide Shaw, DeBERTa and
+  // Transformer-XL and for eight-wave workgroups)
+  {
+    const int by_regs = (p->d > 64 && p->kind != RELATTN_T5 && p->kind != RELATTN_ALIBI) ? 1 : 8 / var.nw;
+    const int by_lds = lds_total > 0 ? kLdsPerCU / lds_total : by_regs;
+    P->cu_slots = std::max(1, std::min(by_regs, by_lds));
+  }
 
   size_t off = 0;
   P->off_part_o = P->off_part_ml = P->off_colc = 0;
@@ -314,6 +322,10 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
   a.scale_log2 = P.scale * 1.4426950408889634f;
   a.n_qtiles = P.n_qtiles;
   a.n_splits = P.n_splits;
+  a.grid = P.grid;
+  a.cu_slots = P.cu_slots;
+  // without a causal mask a workgroup's work is its sequence's valid length
+  a.sort_items = (p->kv_valid_len != nullptr && !p->causal && p->B > 1 && p->B <= kMaxSortSeqs) ? 1 : 0;
   if (P.n_splits > 1) {
     a.part_o = reinterpret_cast<float*>(ws + P.off_part_o);
     a.part_ml = reinterpret_cast<float*>(ws + P.off_part_ml);

@@ -24,6 +24,9 @@ constexpr int kT5MaxThr = 128;   // slots - exact <= 128  (num_buckets <= 256)
 constexpr int kT5MaxLut = 4096;  // entries of the per-head offset -> bias table
 constexpr int kShawMaxK = 32;
 constexpr int kMaxSplits = 32;
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs of 32 CUs
+constexpr int kCuPerXcd = 32;
+constexpr int kMaxSortSeqs = 64;  // sequences a workgroup orders by valid length (one wave)
 constexpr int kLdsPerCU = 160 * 1024;
 
 // Kernel argument block (passed by value).
@@ -43,6 +46,9 @@ struct FwdArgs {
   float scale;      // multiplies the raw score
   float scale_log2; // scale * log2(e)
   int32_t n_qtiles, n_splits;
+  int32_t grid;          // workgroups of this launch
+  int32_t cu_slots;      // workgroups of this launch one CU holds at once
+  int32_t sort_items;    // order work by sequence valid length (non-causal, B <= 64)
   // T5 bucket thresholds and the offset lookup table geometry
   int32_t t5_slots, t5_exact, t5_bidir, t5_nthr;
   int32_t t5_lsat, t5_rsat;  // offsets <= -lsat / >= rsat share one bucket

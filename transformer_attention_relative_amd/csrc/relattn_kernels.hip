@@ -512,6 +512,46 @@ __device__ __forceinline__ f32x16 mma_keyconst(const KeyConst<BF>& kc, int side,
   }
 }
 
+// Work item of the workgroup dispatched at position i of n.  The dispatcher
+// sends workgroup i to XCD i % 8 and, within the XCD, its k-th workgroup
+// (k = i / 8) to CU k % 32, a second round of workgroups taking the CUs'
+// second slots in the same order.  With two slots per CU and m workgroups
+// on an XCD, 32 < m <= 64, the workgroups at k < m - 32 and k >= 32 share
+// a CU while those at m - 32 <= k < 32 run alone.  Items come in order of
+// decreasing work (t = 0 the heaviest of the XCD's items): the heaviest
+// 64 - m run alone, and each shared CU pairs one of the next heaviest with
+// one of the lightest (measured on the padded T5 encoder: 20.1 -> 17.6 us).
+// Otherwise positions map to items in order.
+__device__ __forceinline__ int dispatch_to_item(int i, int n, int cu_slots) {
+  const int x = i % kNumXcd, k = i / kNumXcd;
+  const int m = (n - x + kNumXcd - 1) / kNumXcd;  // workgroups on this XCD
+  int t = k;
+  if (cu_slots == 2 && m > kCuPerXcd && m <= 2 * kCuPerXcd) {
+    if (k < m - kCuPerXcd) t = k + 2 * kCuPerXcd - m;    // shared CU, heavier item
+    else if (k < kCuPerXcd) t = k - (m - kCuPerXcd);     // alone
+    else t = kCuPerXcd + m - 1 - k;                      // shared CU, lighter item
+  }
+  return t * kNumXcd + x;
+}
+
+// The sequence at place `place` when sequences are ordered by valid length
+// (clamped to [0, Lk]) in whole key tiles, most first, ties in index order,
+// and its valid length as given.  One wave: lane j holds sequence j
+// (B <= 64); wave-uniform result.
+__device__ __forceinline__ int2 seq_by_length(const int32_t* len, int B, int Lk, int place) {
+  const int ln = threadIdx.x & 63;
+  const int given = ln < B ? len[ln] : 0;
+  const int tiles = ln < B ? (min(max(given, 0), Lk) + kBK - 1) / kBK : -1;
+  int mine = 0;
+  for (int j = 0; j < B; ++j) {
+    const int tj = __builtin_amdgcn_readlane(tiles, j);
+    mine += (tj > tiles || (tj == tiles && j < ln)) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(ln < B && mine == place);
+  const int b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  return make_int2(b, __builtin_amdgcn_readlane(given, b));
+}
+
 // Workgroups per CU the register budget is set for: two, except where the
 // LDS of a 128-wide head already allows only one (Shaw, DeBERTa, TXL), which
 // then gets the whole register file.
@@ -537,14 +577,33 @@ void relattn_fwd_kernel(FwdArgs a) {
   float* relf = reinterpret_cast<float*>(smem + L.rel_off);
 
   // ---- work item -------------------------------------------------------------
-  // Workgroups are dispatched in id order, round-robin over the 8 XCDs.  The
-  // query-tile rank is the major index, heaviest (latest causal) tiles first,
-  // so every XCD starts its longest items first; (head, split) is the minor
-  // index, so when B*H*splits is a multiple of 8 every item of one (head,
-  // split) lands on the same XCD and shares its L2.
+  // Work items in order of decreasing work: the query-tile rank is the
+  // major index, heaviest (latest causal) tiles first, so every XCD starts
+  // its longest items first.  (head, split) is the minor index, so when
+  // B*H*splits is a multiple of 8 every item of one (head, split) lands on
+  // the same XCD and shares its L2.  Without a causal mask and with
+  // per-sequence valid lengths, the sequences, longest first, are the major
+  // index instead, and the dispatch positions are rearranged so that the
+  // heaviest items get a CU to themselves (see dispatch_to_item).
   const int per_rank = a.B * a.H * a.n_splits;
-  const int rank = blockIdx.x / per_rank;
-  const int rest = blockIdx.x - rank * per_rank;
+  int item = blockIdx.x;
+  int seq_len = -1;  // the sequence's valid length when read here
+  // (one query block per wave: the two-block kernels are chosen for many
+  // workgroups per CU, where the order matters little and registers are short)
+  if (QB == 1 && a.sort_items) {
+    item = dispatch_to_item(blockIdx.x, a.grid, a.cu_slots);
+    // sequences ordered by valid length (the whole work of a workgroup
+    // without a causal mask), sequence-major
+    const int per_pair = a.H * a.n_splits;
+    const int per_seq = a.n_qtiles * per_pair;
+    const int place = item / per_seq;
+    const int r = item - place * per_seq;
+    const int2 bl = seq_by_length(a.kv_valid_len, a.B, a.Lk, place);
+    seq_len = bl.y;
+    item = (r / per_pair) * per_rank + bl.x * per_pair + r % per_pair;
+  }
+  const int rank = item / per_rank;
+  const int rest = item - rank * per_rank;
   const int bh = rest / a.n_splits;
   const int split = rest - bh * a.n_splits;
   const int qt = a.n_qtiles - 1 - rank;
@@ -615,7 +674,8 @@ void relattn_fwd_kernel(FwdArgs a) {
   }
 
   // ---- register loads (valid length, Q fragments, the kind's small tables)
-  const int kv_valid = a.kv_valid_len ? __builtin_amdgcn_readfirstlane(a.kv_valid_len[b]) : a.Lk;
+  const int kv_valid = seq_len >= 0 ? seq_len
+                       : (a.kv_valid_len ? __builtin_amdgcn_readfirstlane(a.kv_valid_len[b]) : a.Lk);
   QFrag qf[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
