@@ -659,18 +659,22 @@ void relattn_fwd_kernel(FwdArgs a) {
   // a per-sequence valid length
   const bool early_copies =
       KIND == 3 ? a.kv_valid_len == nullptr : (a.n_splits == 1 || a.kv_valid_len == nullptr);
+  // Only the first tile goes out here; the others follow the register loads
+  // below.  Memory loads retire in order, so a wait for those registers
+  // would otherwise also wait for every tile issued before them (with four
+  // stages, three tiles of every workgroup at once at kernel start).
+  int early_n0 = 0, early_beg0 = 0;
   if (early_copies) {
     const int n_kt0 = (causal_end + kBK - 1) / kBK;
     const int per0 = (n_kt0 + a.n_splits - 1) / a.n_splits;
-    const int beg0 = min(n_kt0, split * per0);
-    const int n0 = min(n_kt0, beg0 + per0) - beg0;
-    Dma dma;
-    dma.init(wave, lane);
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < n0)
-        dma.issue(Kg, Vg, a.Lk, tile_at(s, beg0, beg0 + n0) * kBK, smem + s * L.stage_bytes,
-                  L.tile_bytes, wave, lane);
+    early_beg0 = min(n_kt0, split * per0);
+    early_n0 = min(n_kt0, early_beg0 + per0) - early_beg0;
+    if (early_n0 > 0) {
+      Dma dma;
+      dma.init(wave, lane);
+      dma.issue(Kg, Vg, a.Lk, tile_at(0, early_beg0, early_beg0 + early_n0) * kBK, smem,
+                L.tile_bytes, wave, lane);
+    }
   }
 
   // ---- register loads (valid length, Q fragments, the kind's small tables)
@@ -765,6 +769,21 @@ void relattn_fwd_kernel(FwdArgs a) {
   const int kt_begin = min(n_kt, split * per_split);
   const int kt_end = min(n_kt, kt_begin + per_split);
   const int n_my = kt_end - kt_begin;
+
+  // ---- the rest of the early tile copies, once the registers' loads (and
+  // the first tile) have landed
+  if constexpr (NS > 2) {
+    if (early_copies && early_n0 > 1) {
+      wait_vmcnt<0>();
+      Dma dma;
+      dma.init(wave, lane);
+#pragma unroll
+      for (int s = 1; s < NS - 1; ++s)
+        if (s < early_n0)
+          dma.issue(Kg, Vg, a.Lk, tile_at(s, early_beg0, early_beg0 + early_n0) * kBK,
+                    smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
+    }
+  }
 
   // ---- per-kind prologue (LDS tables) ---------------------------------------
   float shaw_right[QB];                              // Shaw: q.(a_K[2k] - a_K[0])
