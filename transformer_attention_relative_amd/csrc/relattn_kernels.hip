@@ -698,6 +698,11 @@ void relattn_fwd_kernel(FwdArgs a) {
   // (coalesced) here and written transposed into LDS by the prologue
   constexpr int AVT_CH = (63 * (D / 8) + 64 * NW - 1) / (64 * NW);
   bf16x8 avt_ch[KIND == 1 && BF ? AVT_CH : 1];
+  // Shaw: a_V rows 0 and 2k for this wave's epilogue copy, element e = lane
+  // + 64 * c of [row 0 | row 2k] (read with the other register loads, so no
+  // later step waits for memory)
+  constexpr int AVE = (2 * D + 63) / 64;
+  T av_end[KIND == 1 ? AVE : 1];
   if constexpr (KIND == 0) {
     const float* tab = reinterpret_cast<const float*>(a.table);
 #pragma unroll
@@ -728,6 +733,14 @@ void relattn_fwd_kernel(FwdArgs a) {
         const int e = tid + c * 64 * NW;
         avt_ch[c] = bf16x8{};
         if (e < nch) avt_ch[c] = *reinterpret_cast<const bf16x8*>(av + (size_t)(e / (D / 8) + 1) * D + 8 * (e % (D / 8)));
+      }
+    }
+    {
+      const T* av = reinterpret_cast<const T*>(a.table2);
+#pragma unroll
+      for (int c = 0; c < AVE; ++c) {
+        const int e = lane + 64 * c;
+        av_end[c] = e < 2 * D ? av[(size_t)(e < D ? 0 : 2 * ck) * D + (e % D)] : (T)0.f;
       }
     }
   } else if constexpr (KIND == 2) {
@@ -859,9 +872,10 @@ void relattn_fwd_kernel(FwdArgs a) {
     }
     // this wave's copy of a_V rows 0 and 2k, read by its epilogue
     {
-      const T* av = reinterpret_cast<const T*>(a.table2);
       T* ends = reinterpret_cast<T*>(smem + L.rel_off + L.avend_off) + wave * 2 * D;
-      for (int e = lane; e < 2 * D; e += 64) ends[e] = av[(size_t)(e < D ? 0 : 2 * ck) * D + (e % D)];
+#pragma unroll
+      for (int c = 0; c < AVE; ++c)
+        if (lane + 64 * c < 2 * D) ends[lane + 64 * c] = av_end[c];
     }
     wave_lds_fence();
 #pragma unroll
@@ -1654,13 +1668,19 @@ void relattn_fwd_kernel(FwdArgs a) {
       const float lr_tot = lr_run[qb] + __shfl_xor(lr_run[qb], 32);
       const float w_in = win_run[qb] + __shfl_xor(win_run[qb], 32);
       const float w0 = l_tot - w_in - lr_tot;
+      // register 4g + q of a lane holds head dim 32 db + 8 g + 4 hh + q: four
+      // consecutive elements of each end row, one vector read each
+      using T4 = typename std::conditional<BF, bf16x4, f32x4>::type;
       const T* ends = reinterpret_cast<const T*>(smem + L.rel_off + L.avend_off) + wave * 2 * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int dd = 32 * db + acc_row(i, hh);
-          o[qb][db][i] += w0 * (float)ends[dd] + lr_tot * (float)ends[D + dd];
+        for (int g = 0; g < 4; ++g) {
+          const int dd = 32 * db + 8 * g + 4 * hh;
+          const T4 e0 = *reinterpret_cast<const T4*>(ends + dd);
+          const T4 e1 = *reinterpret_cast<const T4*>(ends + D + dd);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[qb][db][4 * g + q] += w0 * (float)e0[q] + lr_tot * (float)e1[q];
         }
     }
     if (qrow[qb] >= a.Lq) continue;
