@@ -207,6 +207,31 @@ def time_steps(step, steps: int, warmup: int, use_graph: bool):
     return t0.elapsed_time(t1) / steps, wall * 1e3 / steps, graph is not None
 
 
+def time_cold(step, reps: int = 20, flush_bytes: int = 512 << 20):
+    """Median ms of single steps, each after a 512 MiB write that evicts the
+    inputs from L2 and the 256 MiB MALL (they stay resident in HBM).  The
+    step and its events are queued behind the flush, so the events time the
+    step alone."""
+    import torch
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        buf.fill_(1.0)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    del buf
+    return float(np.median(times))
+
+
+COLD = ["t5_encoder_padded", "t5_decoder_kvcache"]   # the HBM-bound workloads
+
+
 def roofline(wl: Workload, flops: float, nbytes: float, ms: float, traffic):
     peak_t = PEAK_TFLOPS[wl.dtype]
     t_mfma = flops / (peak_t * 1e12)
@@ -264,12 +289,13 @@ def cpu_baseline(wl: Workload, inp, budget_s: float = 10.0):
 
 # ----------------------------------------------------------------------------
 
-def measure(name: str, steps: int, warmup: int, use_graph: bool):
+def measure(name: str, steps: int, warmup: int, use_graph: bool, cold: bool = False):
     wl = WORKLOADS[name]
     inp, dev, out, step = _prepare(wl)
     ms, wall_ms, graphed = time_steps(step, steps, warmup, use_graph)
     flops, nbytes = counted_work(wl, inp["kv_valid_len"])
-    return wl, inp, ms, wall_ms, graphed, flops, nbytes
+    cold_ms = time_cold(step) if cold else None
+    return wl, inp, ms, wall_ms, graphed, flops, nbytes, cold_ms
 
 
 def calibrate_copy(nbytes: int, reps: int):
@@ -325,8 +351,8 @@ def main():
         calibrate_copy(args.calibrate_copy, max(args.steps, 1))
         return
 
-    wl, inp, ms, wall_ms, graphed, flops, nbytes = measure(args.workload, args.steps, args.warmup,
-                                                            not args.no_graph)
+    wl, inp, ms, wall_ms, graphed, flops, nbytes, cold_ms = measure(
+        args.workload, args.steps, args.warmup, not args.no_graph, cold=args.workload in COLD)
     tflops = flops / (ms * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
@@ -349,6 +375,10 @@ def main():
                    "host_wall_ms_per_step": round(wall_ms, 5)},
         "roofline": roofline(wl, flops, nbytes, ms, read_traffic(wl.name)),
     }
+    if cold_ms is not None:
+        # single eager steps after an L2 / MALL flush (inputs in HBM only)
+        rec["config"]["cold_ms_per_step"] = round(cold_ms, 5)
+        rec["config"]["cold_hbm_gbs"] = round(nbytes / (cold_ms * 1e-3) / 1e9, 1)
     probe = measured_mfma_peak() if wl.dtype == "bf16" else None
     if probe:
         rec["config"]["mfma_measured_peak_tflops"] = probe
@@ -358,11 +388,15 @@ def main():
         for name in SECONDARY:
             if name == wl.name:
                 continue
-            w2, _, ms2, _, g2, f2, b2 = measure(name, max(10, args.steps // 4), 5, not args.no_graph)
+            w2, _, ms2, _, g2, f2, b2, cold2 = measure(name, max(10, args.steps // 4), 5,
+                                                       not args.no_graph, cold=name in COLD)
             t2 = f2 / (ms2 * 1e-3) / 1e12
             sec[name] = {"tflops": round(t2, 2), "ms_per_step": round(ms2, 5),
                          "mfma_peak_frac": round(t2 / PEAK_TFLOPS[w2.dtype], 4),
                          "roofline": roofline(w2, f2, b2, ms2, read_traffic(name))}
+            if cold2 is not None:
+                sec[name]["cold_ms_per_step"] = round(cold2, 5)
+                sec[name]["cold_hbm_gbs"] = round(b2 / (cold2 * 1e-3) / 1e9, 1)
             if probe and w2.dtype == "bf16":
                 sec[name]["mfma_measured_peak_frac"] = round(t2 / probe, 4)
         rec["secondary"] = sec
