@@ -566,6 +566,11 @@ void relattn_fwd_kernel(FwdArgs a) {
   constexpr int RW = 32 * QB;         // query rows per wave
   constexpr int BQ = RW * NW;         // query rows per workgroup
   constexpr int NS = num_stages(KIND, BF, D);
+  // Four stages go in pairs: one wait, one barrier and two tile copies per
+  // two tiles (the copies of tiles r+2 and r+3 at even r), so each copy
+  // has two tiles of work to land in
+  constexpr bool PAIR = NS == 4;
+  constexpr int AHEAD = PAIR ? 2 : NS - 1;  // tiles copied before the loop
   using Dma = TileDma<BF, D, NW>;
   constexpr int ROWB = Dma::ROWB;     // bytes per K / V row
   constexpr int LPW = Dma::LPW;       // load instructions per wave per tile
@@ -791,7 +796,7 @@ void relattn_fwd_kernel(FwdArgs a) {
       Dma dma;
       dma.init(wave, lane);
 #pragma unroll
-      for (int s = 1; s < NS - 1; ++s)
+      for (int s = 1; s < AHEAD; ++s)
         if (s < early_n0)
           dma.issue(Kg, Vg, a.Lk, tile_at(s, early_beg0, early_beg0 + early_n0) * kBK,
                     smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
@@ -912,7 +917,7 @@ void relattn_fwd_kernel(FwdArgs a) {
     Dma dma;
     dma.init(wave, lane);
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
+    for (int s = 0; s < AHEAD; ++s)
       if (s < n_my)
         dma.issue(Kg, Vg, a.Lk, tile_at(s, kt_begin, kt_end) * kBK, smem + s * L.stage_bytes,
                   L.tile_bytes, wave, lane);
@@ -1059,16 +1064,24 @@ void relattn_fwd_kernel(FwdArgs a) {
     KOffsets<BF, D> ko;
     ko.init(lane);
     const int kt = tile_at(r, kt_begin, kt_end);
-    if constexpr (NS >= 3 && EVEN_LOADS) {
-      // tiles newer than r that may still be in flight: min(NS - 2, n_my - 1 - r)
-      const int newer = min(NS - 2, n_my - 1 - r);
-      if (NS >= 4 && newer >= 2) wait_vmcnt<(NS >= 4 ? 2 * LPW : 0)>();
-      else if (newer >= 1) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
+    if constexpr (PAIR) {
+      // at even r: tiles r and r+1 landed for every wave, every wave is
+      // done with tiles r-2 and r-1
+      if ((r & 1) == 0) {
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
     } else {
-      wait_vmcnt<0>();
+      if constexpr (NS >= 3 && EVEN_LOADS) {
+        // tiles newer than r that may still be in flight: min(NS - 2, n_my - 1 - r)
+        const int newer = min(NS - 2, n_my - 1 - r);
+        if (newer >= 1) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     }
-    __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     const int k0 = kt * kBK;
     // Lean tiles in bfloat16 run as a software pipeline (below); T5 with two
     // query blocks per wave or 128-wide heads keeps the step loop (the
@@ -1077,7 +1090,18 @@ void relattn_fwd_kernel(FwdArgs a) {
     // copies of the tile NS - 1 ahead into the stage of tile r - 1 (free:
     // every wave has passed the barrier above)
     auto issue_next = [&]() {
-      if (r + NS - 1 < n_my) {
+      if constexpr (PAIR) {
+        if ((r & 1) == 0 && r + 2 < n_my) {
+          constexpr bool KEEP = QB == 1 && D <= 64;
+          Dma dma;
+          dma.init(wave, KEEP ? lane : opaque_lane());
+#pragma unroll
+          for (int t = 2; t < 4; ++t)
+            if (r + t < n_my)
+              dma.issue(Kg, Vg, a.Lk, tile_at(r + t, kt_begin, kt_end) * kBK,
+                        smem + ((r + t) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
+        }
+      } else if (r + NS - 1 < n_my) {
         // copy offsets: kept in registers across tiles with one query block
         // per wave; recomputed from a fresh lane id where registers are
         // short (two query blocks, 128-wide heads, DeBERTa's four-wave
