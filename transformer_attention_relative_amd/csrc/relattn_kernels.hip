@@ -387,16 +387,21 @@ __device__ __forceinline__ void lds_dma16_s(const char* gbase, int goff, const c
 // 1 KiB block: row ins*RPI + l/CPR, slot l%CPR, which holds chunk
 // slot ^ swz(row).  The per-lane offsets are fixed; a tile that runs past
 // the last key re-reads the last key for those rows (in bounds; the keys are
-// masked).
+// masked).  Both swizzles read row bits 0..4 only, so when a wave's
+// successive instructions are a multiple of 32 rows apart their per-lane
+// offsets repeat: one (K, V) offset pair per lane then serves every
+// instruction, and the row step goes into the wave-uniform base.
 template <bool BF, int D, int NW>
 struct TileDma {
   static constexpr int ESZ = BF ? 2 : 4, ROWB = D * ESZ, CPR = ROWB / 16;
   static constexpr int RPI = 64 / CPR, IPT = kBK / RPI, IPW = (IPT + NW - 1) / NW;
   static constexpr int LPW = 2 * IPW;  // load instructions per wave per tile
-  int ko[IPW], vo[IPW];
+  static constexpr bool REPEAT = (NW * RPI) % 32 == 0;
+  static constexpr int NOFF = REPEAT ? 1 : IPW;
+  int ko[NOFF], vo[NOFF];
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int r = 0; r < IPW; ++r) {
+    for (int r = 0; r < NOFF; ++r) {
       const int row = (wave + r * NW) * RPI + lane / CPR, slot = lane % CPR;
       ko[r] = row * ROWB + ((slot ^ swz_k<CPR>(row)) * 16);
       vo[r] = row * ROWB + ((slot ^ swz_v<CPR, BF>(row)) * 16);
@@ -410,21 +415,25 @@ struct TileDma {
 #pragma unroll
       for (int r = 0; r < IPW; ++r) {
         const int ins = wave + r * NW;
-        if (ins < IPT) {
-          lds_dma16_s(kb, ko[r], stage + ins * 1024);
-          lds_dma16_s(vb, vo[r], stage + tile_bytes + ins * 1024);
+        const int o = REPEAT ? 0 : r;
+        const int step = REPEAT ? r * NW * RPI * ROWB : 0;  // bytes of the row step
+        if (IPT % NW == 0 || ins < IPT) {  // wave < NW
+          lds_dma16_s(kb + step, ko[o], stage + ins * 1024);
+          lds_dma16_s(vb + step, vo[o], stage + tile_bytes + ins * 1024);
         }
       }
     } else {
 #pragma unroll
       for (int r = 0; r < IPW; ++r) {
         const int ins = wave + r * NW;
-        if (ins < IPT) {
+        const int o = REPEAT ? 0 : r;
+        const int step = REPEAT ? r * NW * RPI * ROWB : 0;
+        if (IPT % NW == 0 || ins < IPT) {  // wave < NW
           const int row = ins * RPI + lane / CPR;
           const int grow = min(k0 + row, Lk - 1);
-          const long long shift = (long long)(grow - row) * ROWB;  // may be negative
-          lds_dma16(Kg + shift + ko[r], stage + ins * 1024);
-          lds_dma16(Vg + shift + vo[r], stage + tile_bytes + ins * 1024);
+          const long long shift = (long long)(grow - row) * ROWB + step;  // may be negative
+          lds_dma16(Kg + shift + ko[o], stage + ins * 1024);
+          lds_dma16(Vg + shift + vo[o], stage + tile_bytes + ins * 1024);
         }
       }
     }
@@ -570,6 +579,8 @@ void relattn_fwd_kernel(FwdArgs a) {
   // two tiles (the copies of tiles r+2 and r+3 at even r), so each copy
   // has two tiles of work to land in
   constexpr bool PAIR = NS == 4;
+  // ring stage of tile r (r >= 0)
+  auto stage_of = [](const int r) -> int { return (int)((unsigned)r % (unsigned)NS); };
   constexpr int AHEAD = PAIR ? 2 : NS - 1;  // tiles copied before the loop
   using Dma = TileDma<BF, D, NW>;
   constexpr int ROWB = Dma::ROWB;     // bytes per K / V row
@@ -1099,7 +1110,7 @@ void relattn_fwd_kernel(FwdArgs a) {
           for (int t = 2; t < 4; ++t)
             if (r + t < n_my)
               dma.issue(Kg, Vg, a.Lk, tile_at(r + t, kt_begin, kt_end) * kBK,
-                        smem + ((r + t) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
+                        smem + stage_of(r + t) * L.stage_bytes, L.tile_bytes, wave, lane);
         }
       } else if (r + NS - 1 < n_my) {
         // copy offsets: kept in registers across tiles with one query block
@@ -1110,7 +1121,7 @@ void relattn_fwd_kernel(FwdArgs a) {
         Dma dma;
         dma.init(wave, KEEP ? lane : opaque_lane());
         dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
-                  smem + ((r + NS - 1) % NS) * L.stage_bytes, L.tile_bytes, wave, lane);
+                  smem + stage_of(r + NS - 1) * L.stage_bytes, L.tile_bytes, wave, lane);
       }
     };
     // a pipelined tile issues them after its first scores, so that its
@@ -1121,7 +1132,7 @@ void relattn_fwd_kernel(FwdArgs a) {
       if (r + 1 < n_my) ring_fill(-64 * (kt + 1), lane);
     }
     if constexpr (CLS == 3) return;
-    const char* ktile = smem + (r % NS) * L.stage_bytes;
+    const char* ktile = smem + stage_of(r) * L.stage_bytes;
     const char* vtile = ktile + L.tile_bytes;
 
     // ---- the tile's query blocks (wave-uniform) ----
