@@ -977,6 +977,13 @@ void relattn_fwd_kernel(FwdArgs a) {
   // as is while every block keeps its lane sums below kSumLimit.
   f32x16 o[QB][NDB];
   float m_ref[QB], l_run[QB], lr_run[QB], win_run[QB];
+  // Transformer-XL (encoding rows from the LDS ring): a wave visits its key
+  // blocks in ascending order, so the first half of a block's band (distances
+  // T0 .. T0+31) is the second half of the next block's; it stays in
+  // registers, tagged with its T0
+  constexpr bool TXL_CARRY = KIND == 4 && KR_RING;
+  f32x16 txl_half[1];
+  int txl_t0 = -(1 << 30);  // no block yet
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -1270,22 +1277,43 @@ void relattn_fwd_kernel(FwdArgs a) {
           float* band = relf + wave * L.deb_wave_floats;
           const T* enc = reinterpret_cast<const T*>(a.table);
           const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
-          TableFrag<BF, D> ef[2];
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {  // negative distances are hidden keys: any row serves
-            if constexpr (KR_RING) {
-              ef[tb].load_lds(ring + ring_slot(T0 + 32 * tb - ring_c0) * 128, ko.k);
-            } else {
-              ef[tb].load(enc + ((size_t)min(max(T0 + 32 * tb + lq, 0), ck - 1) * a.H + h) * D, hh);
+          f32x16 half[2];
+          if constexpr (TXL_CARRY) {
+            // the previous block's first half is this block's second half
+            const bool carried = txl_t0 == T0 + 32;
+            {
+              TableFrag<BF, D> ef;
+              ef.load_lds(ring + ring_slot(T0 - ring_c0) * 128, ko.k);
+              half[0] = mma_frag0<BF, D>(ef, qv[qb]);
             }
+            if (carried) {
+              half[1] = txl_half[0];
+            } else {
+              TableFrag<BF, D> ef;
+              ef.load_lds(ring + ring_slot(T0 + 32 - ring_c0) * 128, ko.k);
+              half[1] = mma_frag0<BF, D>(ef, qv[qb]);
+            }
+            txl_half[0] = half[0];
+            txl_t0 = T0;
+          } else {
+            TableFrag<BF, D> ef[2];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {  // negative distances are hidden keys: any row serves
+              if constexpr (KR_RING) {
+                ef[tb].load_lds(ring + ring_slot(T0 + 32 * tb - ring_c0) * 128, ko.k);
+              } else {
+                ef[tb].load(enc + ((size_t)min(max(T0 + 32 * tb + lq, 0), ck - 1) * a.H + h) * D, hh);
+              }
+            }
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) half[tb] = mma_frag0<BF, D>(ef[tb], qv[qb]);
           }
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
-            const f32x16 acc = mma_frag0<BF, D>(ef[tb], qv[qb]);
             float* dst = band + lq * kCbandStride + 32 * tb + 4 * hh;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+              const f32x4 x = {half[tb][4 * g], half[tb][4 * g + 1], half[tb][4 * g + 2], half[tb][4 * g + 3]};
               *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
             }
           }
