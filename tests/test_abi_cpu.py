@@ -131,6 +131,9 @@ def test_workspace_sizes():
                 causal=1, bidirectional=0)
     n = ra.relattn_workspace_bytes(p)
     assert n >= 2 * 64 * 128 * (64 + 2) * 4 and n % 256 == 0
+    # a 128-row query tile aims at one workgroup per CU: 64 heads x 4 key
+    # parts, each part holding (output, max, sum) per row in float32
+    assert n == 4 * 64 * 128 * (64 + 2) * 4
     # ALiBi and Transformer-XL need no per-key pass; a one-token decode step
     # splits its key range
     p = _params(kind="alibi", table=FAKE, B=4, H=16, Lq=4096, Lk=4096, causal=1)
@@ -142,6 +145,8 @@ def test_workspace_sizes():
                 k_pos_offset=1024, causal=1)
     n = ra.relattn_workspace_bytes(p)
     assert n >= 2 * 64 * 1 * (64 + 2) * 4 and n % 256 == 0
+    # a one-token step aims at two workgroups per CU: 8 key parts
+    assert n == 8 * 64 * 1 * (64 + 2) * 4
     # 128-wide heads in bfloat16 (enough workgroups: no split)
     p = _params(kind="shaw", table=FAKE, table2=FAKE, clip_k=16, d=128, B=4, H=16, Lq=2048,
                 Lk=2048, causal=1)
