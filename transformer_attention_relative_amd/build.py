@@ -35,6 +35,9 @@ HIPCC_FLAGS = [
     # no NaNs in the kernels' arithmetic (scores are finite or -inf): fmaxf
     # then maps to v_max / v_max3 without quieting each operand first
     "-fno-honor-nans",
+    # an inline-assembly diagnostic (e.g. a clobbered register the compiler
+    # reserves) fails the build
+    "-Werror=inline-asm",
     "-Wno-unused-command-line-argument",
 ]
 

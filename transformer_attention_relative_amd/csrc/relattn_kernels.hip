@@ -361,25 +361,46 @@ __device__ __forceinline__ float load_v_f32(const char* vtile, int kb, int cc, i
 
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
 // writes LDS bytes lds_base + 16*l .. +15; lds_base must be wave-uniform.
-// Issued through inline asm so that the compiler does not treat the copy as
-// a pending LDS store that every later LDS read must wait for; the kernel
-// orders it itself (s_waitcnt vmcnt + a workgroup barrier before any read).
+// The copy takes its LDS address from m0.  It is issued from inline assembly
+// that saves m0, sets it, issues the copy and restores it, so m0 holds the
+// compiler's value again when the block ends (no register the compiler
+// reserves is clobbered).  Assembly rather than __builtin_amdgcn_global_load_lds:
+// the compiler cannot tell the copies of the next tile from the tile being
+// read, and with the builtin it waits for every copy in flight
+// (s_waitcnt vmcnt(0)) before each LDS transpose read of V, which serialises
+// the copies with the compute.  The kernel orders the copies itself
+// (s_waitcnt vmcnt for the copies of the tile about to be read, then a
+// workgroup barrier before any wave reads it).
 __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds_base) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const RA_LDS char*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(m0)
-               : "memory", "m0");
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const RA_LDS char*)lds_base;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(m0v)
+      : "memory");
 }
 
 // Same copy with a wave-uniform 64-bit global base and a per-lane 32-bit
 // offset (the scalar-base form: the per-tile address update is scalar).
 __device__ __forceinline__ void lds_dma16_s(const char* gbase, int goff, const char* lds_base) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const RA_LDS char*)lds_base;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(goff), "s"(gbase), "s"(m0)
-               : "memory", "m0");
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const RA_LDS char*)lds_base;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(goff), "s"(gbase), "s"(m0v)
+      : "memory");
 }
 
 // Direct global -> LDS loads of one K tile and one V tile.  Instruction `ins`
