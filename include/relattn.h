@@ -41,8 +41,11 @@
  *           bias u, projected relative encodings E = W_KR R(i - j) against
  *           the query plus the global position bias v.  Causal only (the
  *           cached segment precedes the queries); E has one row per distance
- *           0 .. clip_k - 1 and must cover every visible distance.  The sums
- *           q + u and q + v are rounded to the input type.
+ *           0 .. clip_k - 1 and must cover every visible distance.  The bias
+ *           terms u.k_j (one per key) and v.E[r] (one per distance) are
+ *           formed in float32 by a pre-pass over K and E and added to the
+ *           score as constants; q.k_j and q.E[r] come from the inputs as
+ *           given (nothing is rounded before a product).
  *
  * Offset conventions (documented because mixing them swaps past and future,
  * [RPE] "Failure modes"): T5 and Shaw index by key - query; DeBERTa's
@@ -160,8 +163,10 @@ relattn_status relattn_fwd(const relattn_params *p, const void *q, const void *k
                            size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace relattn_fwd needs for this problem: the split-KV
- * partial results of decode-like shapes, and for DEBERTA the per-key
- * position-to-content constants of clipped blocks (8 bytes per key). */
+ * partial results of decode-like shapes; for DEBERTA the per-key
+ * position-to-content constants of clipped blocks (8 bytes per key and
+ * head); for TXL the per-key constants u.k_j (8 bytes per key and head) and
+ * the per-distance constants v.E[r] (8 bytes per encoding row and head). */
 relattn_status relattn_workspace_bytes(const relattn_params *p, size_t *bytes);
 
 /*

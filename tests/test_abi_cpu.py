@@ -134,13 +134,17 @@ def test_workspace_sizes():
     # a 128-row query tile aims at one workgroup per CU: 64 heads x 4 key
     # parts, each part holding (output, max, sum) per row in float32
     assert n == 4 * 64 * 128 * (64 + 2) * 4
-    # ALiBi and Transformer-XL need no per-key pass; a one-token decode step
-    # splits its key range
+    # ALiBi needs no per-key pass; Transformer-XL holds u.k_j per (head, key)
+    # and v.E[r] per (head, encoding row), 8 bytes each, each region rounded
+    # up to 256 bytes; a one-token decode step splits its key range
     p = _params(kind="alibi", table=FAKE, B=4, H=16, Lq=4096, Lk=4096, causal=1)
     assert ra.relattn_workspace_bytes(p) == 0
     p = _params(kind="txl", table=FAKE, table2=FAKE, clip_k=4096, B=4, H=16, Lq=2048,
                 Lk=4096, q_pos_offset=2048, causal=1)
-    assert ra.relattn_workspace_bytes(p) == 0
+    assert ra.relattn_workspace_bytes(p) == 64 * 4096 * 8 + 16 * 4096 * 8
+    p = _params(kind="txl", table=FAKE, table2=FAKE, clip_k=333, B=1, H=3, Lq=130,
+                Lk=330, q_pos_offset=203, causal=1)
+    assert ra.relattn_workspace_bytes(p) == (3 * 330 * 8 + 255) // 256 * 256 + (3 * 333 * 8 + 255) // 256 * 256
     p = _params(kind="alibi", table=FAKE, B=4, H=16, Lq=1, Lk=3072, q_pos_offset=4095,
                 k_pos_offset=1024, causal=1)
     n = ra.relattn_workspace_bytes(p)
@@ -191,3 +195,89 @@ def test_header_abi_version_matches_binding():
     src = open(HEADER).read()
     m = re.search(r"#define RELATTN_ABI_VERSION (\d+)", src)
     assert m and int(m.group(1)) == ra.binding.ABI_VERSION
+
+
+# ----------------------------------------------------------------------------
+# the Python binding checks every tensor before it calls the library (dtype,
+# exact shape per kind as include/relattn.h states it, layout, then device);
+# here the tensors live on the CPU, so the call must stop at a check
+# ----------------------------------------------------------------------------
+
+def _fwd_args(kind="deberta", dtype=None, B=2, H=3, Lq=5, Lk=7, d=32, k=4):
+    import torch
+    dt = torch.bfloat16 if dtype is None else dtype
+    q = torch.zeros(B, H, Lq, d, dtype=dt)
+    kk = torch.zeros(B, H, Lk, d, dtype=dt)
+    v = torch.zeros(B, H, Lk, d, dtype=dt)
+    tabs = {"t5": (torch.zeros(32, H), None), "alibi": (torch.zeros(H), None),
+            "shaw": (torch.zeros(2 * k + 1, d, dtype=dt), torch.zeros(2 * k + 1, d, dtype=dt)),
+            "deberta": (torch.zeros(2 * k, H, d, dtype=dt), torch.zeros(2 * k, H, d, dtype=dt)),
+            "txl": (torch.zeros(k, H, d, dtype=dt), torch.zeros(2, H, d, dtype=dt))}[kind]
+    return q, kk, v, tabs[0], tabs[1], dict(clip_k=k)
+
+
+@pytest.mark.parametrize("kind", ["t5", "alibi", "shaw", "deberta", "txl"])
+def test_binding_wellformed_cpu_tensors_stop_at_the_device_check(kind):
+    q, k, v, t1, t2, kw = _fwd_args(kind)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ra.relattn_fwd(q, k, v, kind, t1, t2, **kw)
+
+
+@pytest.mark.parametrize("case", [
+    "k_dtype", "v_shape", "table_shape", "table_dtype", "table2_missing", "table2_extra",
+    "table2_shape", "lens_dtype", "lens_short", "lse_shape", "lse_dtype", "out_shape",
+    "out_dtype", "out_layout", "q_3d", "bad_kind", "t5_buckets"])
+def test_binding_rejects_malformed_tensors(case):
+    import torch
+    kind = "t5" if case == "t5_buckets" else ("shaw" if case == "table2_extra" else "deberta")
+    q, k, v, t1, t2, kw = _fwd_args(kind)
+    extra = {}
+    if case == "k_dtype":
+        k = k.float()
+    elif case == "v_shape":
+        v = v[:, :, :-1].contiguous()
+    elif case == "table_shape":
+        t1 = t1[:-1].contiguous()            # 2k - 1 rows
+    elif case == "table_dtype":
+        t1 = t1.float()
+    elif case == "table2_missing":
+        t2 = None
+    elif case == "table2_extra":
+        kind = "alibi"
+        t1, t2 = torch.zeros(q.shape[1]), t2
+    elif case == "table2_shape":
+        t2 = torch.zeros(2 * kw["clip_k"], q.shape[1] + 1, q.shape[3], dtype=q.dtype)
+    elif case == "lens_dtype":
+        extra["kv_valid_len"] = torch.zeros(q.shape[0], dtype=torch.int64)
+    elif case == "lens_short":
+        extra["kv_valid_len"] = torch.zeros(q.shape[0] - 1, dtype=torch.int32)
+    elif case == "lse_shape":
+        extra["lse"] = torch.zeros(q.shape[:3][::-1], dtype=torch.float32)
+    elif case == "lse_dtype":
+        extra["lse"] = torch.zeros(q.shape[:3], dtype=torch.bfloat16)
+    elif case == "out_shape":
+        extra["out"] = torch.zeros(q.shape[0], q.shape[1], q.shape[2] + 1, q.shape[3], dtype=q.dtype)
+    elif case == "out_dtype":
+        extra["out"] = torch.zeros(q.shape, dtype=torch.float32)
+    elif case == "out_layout":
+        extra["out"] = torch.zeros(q.shape[::-1], dtype=q.dtype).permute(3, 2, 1, 0)
+    elif case == "q_3d":
+        q = q[0]
+    elif case == "bad_kind":
+        kind = "rope"
+    elif case == "t5_buckets":
+        kw["num_buckets"] = 64                # table has 32 rows
+    with pytest.raises((TypeError, ValueError)) as e:
+        ra.relattn_fwd(q, k, v, kind, t1, t2, **kw, **extra)
+    assert "GPU tensor" not in str(e.value)
+
+
+def test_binding_rel_index_checks():
+    import torch
+    qp = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="shape"):
+        ra.relattn_rel_index("t5", qp, torch.zeros(7, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        ra.relattn_rel_index("t5", qp, torch.zeros(8, dtype=torch.int64))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ra.relattn_rel_index("t5", qp, qp.clone())

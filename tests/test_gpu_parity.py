@@ -29,10 +29,48 @@ def _to_dev(inp):
     return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
 
 
-def run_gpu(wl: Workload, dev_inp):
-    out = ra.relattn_fwd(dev_inp["q"], dev_inp["k"], dev_inp["v"], wl.kind, dev_inp["table"],
-                         dev_inp["table2"], kv_valid_len=dev_inp["kv_valid_len"], **params_of(wl))
+GUARD = 4096          # bytes of sentinel on each side of every output buffer
+SENTINEL = 0xA5
+
+
+def _guarded(nbytes):
+    """A byte buffer with GUARD sentinel bytes before and after `nbytes`
+    (the middle starts 4 KiB-aligned, so every view is 16-byte aligned)."""
+    buf = torch.full((2 * GUARD + max(nbytes, 0),), SENTINEL, dtype=torch.uint8, device=DEV)
+    return buf, buf[GUARD:GUARD + nbytes]
+
+
+def _check_guards(buf, what):
+    lo, hi = buf[:GUARD], buf[-GUARD:]
+    assert bool((lo == SENTINEL).all()) and bool((hi == SENTINEL).all()), \
+        f"{what}: a kernel wrote outside its buffer"
+
+
+def run_gpu(wl: Workload, dev_inp, lse=False):
+    """The fused forward through the C ABI with `out`, `lse` and the workspace
+    each placed between two 4 KiB sentinel bands, checked after the call."""
+    B, H, Lq, d = dev_inp["q"].shape
+    esz = dev_inp["q"].element_size()
+    p = ra.make_params(wl.kind, wl.dtype, B, H, Lq, dev_inp["k"].shape[2], d,
+                       table=dev_inp["table"], table2=dev_inp["table2"],
+                       kv_valid_len=dev_inp["kv_valid_len"], **params_of(wl))
+    need = ra.relattn_workspace_bytes(p)
+    out_buf, out_b = _guarded(B * H * Lq * d * esz)
+    out = out_b.view(dev_inp["q"].dtype).view(B, H, Lq, d)
+    ws_buf, ws = _guarded(need)
+    lse_buf = lse_t = None
+    if lse:
+        lse_buf, lse_b = _guarded(B * H * Lq * 4)
+        lse_t = lse_b.view(torch.float32).view(B, H, Lq)
+    ra.relattn_fwd(dev_inp["q"], dev_inp["k"], dev_inp["v"], wl.kind, dev_inp["table"],
+                   dev_inp["table2"], kv_valid_len=dev_inp["kv_valid_len"], out=out,
+                   workspace=ws if need else None, lse=lse_t, **params_of(wl))
     torch.cuda.synchronize()
+    _check_guards(out_buf, "out")
+    _check_guards(ws_buf, "workspace")
+    if lse:
+        _check_guards(lse_buf, "lse")
+        return out, lse_t
     return out
 
 
@@ -345,11 +383,7 @@ LSE_TOL = {"fp32": 1e-5, "bf16": 4e-3}
 
 
 def _run_gpu_lse(wl, dev):
-    lse = torch.empty((wl.B, wl.H, wl.Lq), dtype=torch.float32, device=DEV)
-    out = ra.relattn_fwd(dev["q"], dev["k"], dev["v"], wl.kind, dev["table"], dev["table2"],
-                         kv_valid_len=dev["kv_valid_len"], lse=lse, **params_of(wl))
-    torch.cuda.synchronize()
-    return out, lse
+    return run_gpu(wl, dev, lse=True)
 
 
 LSE_CASES = [c for c in SMALL_CASES if c.d == 64 or c.dtype == "fp32"][::3] + DECODE_CASES[::2]
@@ -475,16 +509,22 @@ def _sample_rows(Lq, rng):
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_parity_full_size_sampled(name):
+    # every (batch, head) pair, each on its own sample of query rows (the
+    # fixed tile edges plus random rows), in the benchmark's launch layout
     wl = WORKLOADS[name]
     inp = make_inputs(wl, seed=0)
     got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
-    rng = np.random.default_rng(0)
-    heads = [(0, 0), (wl.B - 1, wl.H - 1), (int(rng.integers(wl.B)), int(rng.integers(wl.H)))]
-    rows = _sample_rows(wl.Lq, rng)
-    want = run_oracle(wl, inp, heads=heads, rows=rows)
-    sel = np.stack([got[b, h][rows] for b, h in heads])
-    check_close(sel, want, wl.dtype, name)
     assert np.isfinite(got).all()
+    rng = np.random.default_rng(0)
+    q, k, v = _np(inp["q"]), _np(inp["k"]), _np(inp["v"])
+    t1, t2 = _np(inp["table"]), _np(inp["table2"])
+    lens = None if inp["kv_valid_len"] is None else inp["kv_valid_len"].numpy()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            rows = _sample_rows(wl.Lq, rng)
+            want = oracle.relattn_forward(q, k, v, wl.kind, t1, t2, kv_valid_len=lens,
+                                          heads=[(b, h)], rows=rows, **params_of(wl))
+            check_close(got[b, h][rows][None], want, wl.dtype, f"{name} b{b} h{h}")
 
 
 # Per-sequence valid lengths without a causal mask: the kernel orders its
@@ -600,6 +640,124 @@ def test_shaw_bins_readout_through_fused_kernel():
         np.testing.assert_allclose(got, want, atol=1e-6)
 
 
+def _logits_readout(kind, q, k, table, table2, *, clip_k, q_pos_offset, causal, scale):
+    """Absolute logits of every (query, key) pair as the fused kernel forms
+    them: V one-hot over a window of 64 keys per call (out[i, c] = p of key
+    w0 + c), and log p + the row LSE = the logit.  d = 64; -inf where hidden."""
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    assert d == 64
+    logits = np.full((B, H, Lq, Lk), -np.inf)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=DEV)
+    for w0 in range(0, Lk, 64):
+        n = min(64, Lk - w0)
+        v = torch.zeros((B, H, Lk, d), dtype=q.dtype, device=DEV)
+        idx = torch.arange(n, device=DEV)
+        v[:, :, w0 + idx, idx] = 1.0
+        out = ra.relattn_fwd(q, k, v, kind, table, table2, clip_k=clip_k, causal=causal,
+                             q_pos_offset=q_pos_offset, scale=scale, lse=lse)
+        torch.cuda.synchronize()
+        p = out[..., :n].double().cpu().numpy()
+        with np.errstate(divide="ignore"):
+            logits[..., w0:w0 + n] = np.log(p) + lse.double().cpu().numpy()[..., None]
+    return logits
+
+
+def _deberta_readout_case(which):
+    # DeBERTa ring kernel (bfloat16, d = 64, clip window >= 64): 300 query
+    # rows (a full and a ragged workgroup of 256 rows) at positions 37..336
+    # against 320 keys: clipped blocks on both sides, window edges (k = 100)
+    # inside tiles.  which = 0 reads d(i, j) through q.Kr[d(i, j)] (Q = e0,
+    # K = 0, Qr = 0); which = 1 reads d(j, i) through k_j.Qr[d(j, i)] (K = e0,
+    # Q = 0, Kr = 0).  Head 1 reads the table in reverse (2k - 1 - row), so a
+    # head mix-up cannot pass.
+    B, H, Lq, Lk, d, kc, qpo = 1, 2, 300, 320, 64, 100, 37
+    bf = torch.bfloat16
+    q = torch.zeros(B, H, Lq, d, dtype=bf, device=DEV)
+    k = torch.zeros(B, H, Lk, d, dtype=bf, device=DEV)
+    (q if which == 0 else k)[..., 0] = 1.0
+    rows = torch.arange(2 * kc, dtype=torch.float32)
+    tab = torch.zeros(2 * kc, H, d)
+    tab[:, 0, 0] = rows / 8                    # exact in bfloat16 (rows < 256)
+    tab[:, 1, 0] = (2 * kc - 1 - rows) / 8
+    tab = tab.to(bf).to(DEV)
+    zero = torch.zeros_like(tab)
+    kr, qr = (tab, zero) if which == 0 else (zero, tab)
+    # logit = scale * row / 8 with scale 2: a quarter per index step
+    logits = _logits_readout("deberta", q, k, kr, qr, clip_k=kc, q_pos_offset=qpo, causal=False,
+                             scale=2.0)
+    want = oracle.rel_index_matrices("deberta", Lq, Lk, q_pos_offset=qpo, clip_k=kc)
+    want = want["idx"] if which == 0 else want["idx2"]
+    return logits, want, kc
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_deberta_delta_readout_through_fused_kernel(which):
+    # [DRPE] "The Relative Position Formula": the clip-and-shift index of
+    # every pair, read back through the ring kernel's band and clipped paths
+    logits, want, kc = _deberta_readout_case(which)
+    assert np.isfinite(logits).all()
+    got = 4 * logits
+    dec = np.rint(got).astype(np.int64)
+    assert np.abs(got - dec).max() < 0.1       # the readout is sharp
+    assert np.array_equal(dec[0, 0], want)
+    assert np.array_equal(dec[0, 1], 2 * kc - 1 - want)
+
+
+def _encode_index(x, d):
+    """[..., d] rows whose first two entries sum to x / 8 (both exact in
+    bfloat16 for 0 <= x < 512): (x - x mod 64) / 8 and (x mod 64) / 8."""
+    x = torch.as_tensor(x, dtype=torch.float32)
+    out = torch.zeros(x.shape + (d,))
+    out[..., 0] = (x - torch.remainder(x, 64)) / 8
+    out[..., 1] = torch.remainder(x, 64) / 8
+    return out
+
+
+@pytest.mark.parametrize("path", ["query", "position_bias", "content_bias"])
+def test_txl_distance_readout_through_fused_kernel(path):
+    # [RPE] "Transformer-XL": the row E[i - j] of every visible pair, read
+    # back through the ring kernel (bfloat16, d = 64, ascending blocks with the
+    # carried half).  path "query": q.E[i - j] (Q = e0 + e1, u = v = 0);
+    # "position_bias": v.E[i - j] (Q = 0, v = e0 + e1), the per-distance
+    # constant; "content_bias": u.k_j with k_j encoding the key index j (Q =
+    # 0, E = 0, u = e0 + e1), the per-key constant.  Head h reads E at row
+    # + 8h (a head mix-up cannot pass).  Queries at 20..319, keys 0..319.
+    B, H, Lq, Lk, d, qpo = 1, 2, 300, 320, 64, 20
+    rows = qpo + Lq                                  # encodings for distances 0..319
+    bf = torch.bfloat16
+    q = torch.zeros(B, H, Lq, d)
+    k = torch.zeros(B, H, Lk, d)
+    enc = torch.zeros(rows, H, d)
+    uv = torch.zeros(2, H, d)
+    r = torch.arange(rows)
+    if path in ("query", "position_bias"):
+        for h in range(H):
+            enc[:, h] = _encode_index(r + 8 * h, d)
+        if path == "query":
+            q[..., 0] = q[..., 1] = 1.0
+        else:
+            uv[1, :, 0] = uv[1, :, 1] = 1.0
+    else:
+        k[...] = _encode_index(torch.arange(Lk), d)
+        uv[0, :, 0] = uv[0, :, 1] = 1.0
+    dev = lambda t: t.to(bf).to(DEV).contiguous()
+    logits = _logits_readout("txl", dev(q), dev(k), dev(enc), dev(uv), clip_k=rows,
+                             q_pos_offset=qpo, causal=True, scale=2.0)
+    dist = oracle.rel_index_matrices("txl", Lq, Lk, q_pos_offset=qpo, clip_k=rows)["idx"]
+    vis = dist >= 0
+    assert np.array_equal(np.isfinite(logits[0, 0]), vis)
+    for h in range(H):
+        got = 4 * logits[0, h][vis]
+        dec = np.rint(got).astype(np.int64)
+        assert np.abs(got - dec).max() < 0.1
+        if path == "content_bias":
+            want = np.broadcast_to(np.arange(Lk), dist.shape)[vis]
+        else:
+            want = dist[vis] + 8 * h
+        assert np.array_equal(dec, want), path
+
+
 # ----------------------------------------------------------------------------
 # 5. the online softmax's reference max: scores that grow along the keys make
 #    it move many times; a late jump far above every earlier score overflows
@@ -643,20 +801,10 @@ RAMP_CASES = [
 STRESS_TOL = {"fp32": (2e-4, 2e-5), "bf16": TOL["bf16"]}
 
 
-def _txl_zero_biases(wl, inp):
-    """Transformer-XL forms q + u and q + v in the input dtype before its
-    products, a rounding the oracle does not make whose effect grows with the
-    logit (about 2^-8 of it in bfloat16: ~0.1 at these stress logits).  Zero
-    biases keep the stress inputs about the running reference alone."""
-    if wl.kind != "txl":
-        return inp
-    return dict(inp, table2=torch.zeros_like(inp["table2"]))
-
-
 @pytest.mark.parametrize("wl", RAMP_CASES, ids=_case_id)
 def test_reference_moves_with_growing_scores(wl):
     # logits grow from ~0 to ~+-45 log2 units along the keys
-    inp = _txl_zero_biases(wl, _ramped(wl, make_inputs(wl, seed=21), 0.05, 6.0, 1.5))
+    inp = _ramped(wl, make_inputs(wl, seed=21), 0.05, 6.0, 1.5)
     got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
     want = run_oracle(wl, inp)
     err = np.abs(got - want)
@@ -679,10 +827,27 @@ def test_late_score_jump_is_exact(kind, two_blocks):
         wl = _small(kind, "bf16", 64, Lq=130, Lk=600, clip_k=16 if kind in ("shaw", "deberta") else 0)
     if two_blocks:
         wl = wl.replace(B=2, H=256, Lq=256)
-    inp = _txl_zero_biases(wl, make_inputs(wl, seed=22))
+    inp = make_inputs(wl, seed=22)
     k = inp["k"].float()
     k[:, :, -40:] *= 12.0
     inp = dict(inp, k=k.to(wl.torch_dtype), q=(inp["q"].float() * 2.0).to(wl.torch_dtype))
     got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
     want = run_oracle(wl, inp)
     check_close(got, want, wl.dtype, f"{kind} jump")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 32), ("fp32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("sigma", [1.0, 3.0])
+def test_txl_large_global_biases(dtype, d, sigma):
+    # u and v as large as the queries themselves (sigma 1) and three times
+    # larger: the bias terms u.k_j and v.E[i - j] are float32 constants, so
+    # the scores keep the inputs' precision ([RPE] "Transformer-XL: four
+    # terms and two global biases": (q_i + u).k_j + (q_i + v).E[i - j])
+    wl = _small("txl", dtype, d, causal=True, Lq=300, Lk=700, q_pos_offset=400, clip_k=700)
+    inp = make_inputs(wl, seed=23)
+    g = torch.Generator("cpu").manual_seed(24)
+    uv = (torch.randn(inp["table2"].shape, generator=g) * sigma).to(wl.torch_dtype)
+    inp = dict(inp, table2=uv)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    want = run_oracle(wl, inp)
+    check_close(got, want, wl.dtype, f"txl biases sigma {sigma}")

@@ -208,6 +208,44 @@ def test_rows_selection_matches_full():
     np.testing.assert_allclose(part[1], full[0, 1, [0, 5, 20]], atol=1e-13)
 
 
+@pytest.mark.parametrize("kind", ["t5", "shaw", "deberta", "alibi", "txl"])
+def test_batched_valid_lengths_equal_truncated_keys(kind):
+    """The batched forward's per-sequence lengths ([T5B]: the padding mask
+    hides key index j >= n_b of sequence b) against the same computation on
+    each sequence's keys cut to its length, with no mask at all.  B != H and
+    every length differs, so taking the length of the wrong sequence (or a
+    head's index for a sequence's) changes the result."""
+    rng = np.random.default_rng(31)
+    B, H, Lq, Lk, d, clip = 3, 2, 9, 14, 8, 3
+    q, k, v = _rand(rng, B, H, Lq, d), _rand(rng, B, H, Lk, d), _rand(rng, B, H, Lk, d)
+    causal, q_off = (True, 10) if kind == "txl" else (False, 4)
+    if kind == "t5":
+        t1, t2 = _rand(rng, 32, H), None
+    elif kind == "alibi":
+        t1, t2 = _rand(rng, H, s=0.3), None
+    elif kind == "txl":
+        t1, t2 = _rand(rng, q_off + Lq, H, d), _rand(rng, 2, H, d)
+    elif kind == "shaw":
+        t1, t2 = _rand(rng, 2 * clip + 1, d), _rand(rng, 2 * clip + 1, d)
+    else:
+        t1, t2 = _rand(rng, 2 * clip, H, d), _rand(rng, 2 * clip, H, d)
+    lens = np.array([5, 14, 1])
+    kw = dict(clip_k=clip, q_pos_offset=q_off, causal=causal)
+    got, lse = oracle.relattn_forward(q, k, v, kind, t1, t2, kv_valid_len=lens,
+                                      return_lse=True, **kw)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(H):
+            want, wl = oracle.relattn_forward_head(q[b, h], k[b, h, :n], v[b, h, :n], kind, h,
+                                                   t1, t2, return_lse=True, **kw)
+            np.testing.assert_allclose(got[b, h], want, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[b, h], wl, atol=1e-12, rtol=0)
+    # and the lengths do matter: the sequences differ from the unmasked run
+    full = oracle.relattn_forward(q, k, v, kind, t1, t2, **kw)
+    assert np.abs(full[0] - got[0]).max() > 1e-3 and np.abs(full[2] - got[2]).max() > 1e-3
+    np.testing.assert_allclose(full[1], got[1], atol=1e-12, rtol=0)
+
+
 # -------------------------------------------------------------- brute force
 
 @settings(max_examples=60, deadline=None)

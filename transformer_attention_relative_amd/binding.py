@@ -9,7 +9,6 @@ raised.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import threading
 from typing import Optional
@@ -126,6 +125,42 @@ def relattn_workspace_bytes(params: relattn_params) -> int:
     return n.value
 
 
+def _table_specs(kind: str, dtype, H: int, d: int, clip_k: int, num_buckets: int):
+    """(dtype, shape) of table and table2 for a kind, as include/relattn.h
+    states them (None: the table must be absent)."""
+    import torch
+    if kind == "t5":
+        return (torch.float32, (num_buckets, H)), None
+    if kind == "alibi":
+        return (torch.float32, (H,)), None
+    if kind == "shaw":
+        n = 2 * clip_k + 1
+        return (dtype, (n, d)), (dtype, (n, d))
+    if kind == "deberta":
+        n = 2 * clip_k
+        return (dtype, (n, H, d)), (dtype, (n, H, d))
+    if kind == "txl":
+        return (dtype, (clip_k, H, d)), (dtype, (2, H, d))
+    raise ValueError(f"unknown kind {kind!r}")
+
+
+def _check_tensor(name, t, dtype=None, shape=None):
+    """dtype and shape first, then contiguity; the device is checked last
+    (by _check_device), so the layout errors show on any machine."""
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != device):
+            raise ValueError(f"{name} must be a GPU tensor on {device} (got {t.device})")
+
+
 def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int = 32,
                 max_distance: int = 128, bidirectional: bool = True, clip_k: int = 0,
                 q_pos_offset: int = 0, k_pos_offset: int = 0, causal: bool = False,
@@ -139,32 +174,53 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
     [2, H, d] (input dtype).  Query row i sits at
     absolute position ``q_pos_offset + i``, key row j at ``k_pos_offset + j``.
     ``kv_valid_len``:
-    int32 [B] on the GPU or None.  ``out`` and ``workspace`` are allocated
-    with torch when not given.  ``lse``: a float32 [B, H, Lq] GPU tensor that
-    receives each row's log-sum-exp of the logits (natural log), or None.
+    int32 [B] on the GPU or None.  ``out`` ([B, H, Lq, d], q's dtype) and
+    ``workspace`` (any dtype, at least ``relattn_workspace_bytes`` bytes) are
+    allocated with torch when not given.  ``lse``: a float32 [B, H, Lq] GPU
+    tensor that receives each row's log-sum-exp of the logits (natural log),
+    or None.  Every tensor's dtype, shape, layout and device is checked here
+    before the library is called.
     """
     import torch
-    lib = load_library()
+    if kind not in KINDS:
+        raise ValueError(f"unknown kind {kind!r}")
     if q.dtype == torch.float32:
         dtype = "fp32"
     elif q.dtype == torch.bfloat16:
         dtype = "bf16"
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
-    for name, t in (("q", q), ("k", k), ("v", v), ("table", table), ("table2", table2),
-                    ("kv_valid_len", kv_valid_len), ("lse", lse)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
-    if kv_valid_len is not None and kv_valid_len.dtype != torch.int32:
-        raise TypeError("kv_valid_len must be int32")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k and v must be 4-D [B, H, L, d]")
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Lq)):
-        raise ValueError("lse must be a float32 [B, H, Lq] tensor")
-    if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
-        raise ValueError("k and v must be [B, H, Lk, d] matching q")
+    _check_tensor("q", q)
+    _check_tensor("k", k, q.dtype, (B, H, Lk, d))
+    _check_tensor("v", v, q.dtype, (B, H, Lk, d))
+    spec1, spec2 = _table_specs(kind, q.dtype, H, d, clip_k, num_buckets)
+    if table is None:
+        raise ValueError(f"{kind} needs table {spec1[1]}")
+    _check_tensor("table", table, *spec1)
+    if spec2 is None:
+        if table2 is not None:
+            raise ValueError(f"{kind} takes no table2")
+    else:
+        if table2 is None:
+            raise ValueError(f"{kind} needs table2 {spec2[1]}")
+        _check_tensor("table2", table2, *spec2)
+    if kv_valid_len is not None:
+        _check_tensor("kv_valid_len", kv_valid_len, torch.int32)
+        if kv_valid_len.numel() < B:
+            raise ValueError(f"kv_valid_len needs {B} entries (got {kv_valid_len.numel()})")
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, (B, H, Lq))
+    if out is not None:
+        _check_tensor("out", out, q.dtype, (B, H, Lq, d))
+    if workspace is not None:
+        _check_tensor("workspace", workspace)
+    _check_device(q.device, q=q, k=k, v=v, table=table, table2=table2,
+                  kv_valid_len=kv_valid_len, lse=lse, out=out, workspace=workspace)
+    lib = load_library()
     p = make_params(kind, dtype, B, H, Lq, Lk, d, table=table, table2=table2,
                     num_buckets=num_buckets, max_distance=max_distance,
                     bidirectional=bidirectional, clip_k=clip_k, q_pos_offset=q_pos_offset,
@@ -187,9 +243,14 @@ def relattn_rel_index(kind: str, q_pos, k_pos, which: int = 0, *, num_buckets: i
                       out=None):
     """Index of each (q_pos[e], k_pos[e]) pair (int32 GPU tensors) on the GPU."""
     import torch
+    if kind not in KINDS:
+        raise ValueError(f"unknown kind {kind!r}")
+    _check_tensor("q_pos", q_pos, torch.int32)
+    _check_tensor("k_pos", k_pos, torch.int32, tuple(q_pos.shape))
+    if out is not None:
+        _check_tensor("out", out, torch.int32, tuple(q_pos.shape))
+    _check_device(q_pos.device, q_pos=q_pos, k_pos=k_pos, out=out)
     lib = load_library()
-    if q_pos.shape != k_pos.shape or q_pos.dtype != torch.int32 or k_pos.dtype != torch.int32:
-        raise ValueError("q_pos and k_pos must be int32 tensors of one shape")
     if out is None:
         out = torch.empty_like(q_pos)
     p = make_params(kind, "fp32", 1, 1, 1, 1, 32, num_buckets=num_buckets,
@@ -209,7 +270,3 @@ def relattn_t5_thresholds(num_buckets: int = 32, max_distance: int = 128,
     _check(lib, lib.relattn_t5_thresholds(num_buckets, max_distance, int(bool(bidirectional)),
                                           buf, 256, ctypes.byref(cnt)))
     return list(buf[: cnt.value])
-
-
-def default_scale(kind: str, d: int) -> float:
-    return 1.0 / math.sqrt(3 * d) if kind == "deberta" else 1.0 / math.sqrt(d)

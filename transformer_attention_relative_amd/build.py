@@ -42,6 +42,9 @@ HIPCC_FLAGS = [
 ]
 
 
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+
 def hipcc_path() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -49,29 +52,40 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librelattn.so)")
 
 
-def _compile(sources, out_path):
-    tmp = out_path + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
+def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
         raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd)}")
-    os.replace(tmp, out_path)
     return proc
+
+
+def compile_object(source: str, extra=()) -> str:
+    """Compile one source of csrc/ to an object under _build/; return its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = os.path.join(BUILD_DIR, os.path.splitext(source)[0] + ".o")
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    _run([hipcc_path(), *flags, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+          "-c", os.path.join(CSRC, source), "-o", obj + ".tmp"])
+    os.replace(obj + ".tmp", obj)
+    return obj
+
+
+def link(objects, out_path, extra=()):
+    tmp = out_path + ".tmp"
+    _run([hipcc_path(), "--offload-arch=gfx950", "-shared", "-fPIC", *extra, *objects, "-o", tmp])
+    os.replace(tmp, out_path)
+    return out_path
 
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP/C++ source for gfx950 (the library and the benchmark's
     MFMA probe); return the library's .so path."""
     t0 = time.time()
-    proc = _compile(SOURCES, LIB_PATH)
-    _compile([PROBE_SOURCE], PROBE_PATH)
+    objs = [compile_object(src) for src in SOURCES]
+    link(objs, LIB_PATH)
+    link([compile_object(PROBE_SOURCE)], PROBE_PATH)
     if verbose:
-        noisy = [l for l in (proc.stdout + proc.stderr).splitlines()
-                 if "packed-fp32-ops" not in l]
-        if noisy:
-            print("\n".join(noisy))
         print(f"built {LIB_PATH} in {time.time() - t0:.1f}s")
     return LIB_PATH
 

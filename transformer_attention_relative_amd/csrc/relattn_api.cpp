@@ -103,7 +103,7 @@ struct Plan {
   float scale;
   Variant var;
   int n_qtiles, n_splits, grid, lds, cu_slots;
-  size_t off_part_o, off_part_ml, off_colc, ws_bytes;
+  size_t off_part_o, off_part_ml, off_colc, off_colc2, ws_bytes;
   T5Plan t5;
 };
 
@@ -242,17 +242,28 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     P->cu_slots = std::max(1, std::min(by_regs, by_lds));
   }
 
+  // the row-constant pre-pass runs one thread per (head, key) and per
+  // (head, encoding row)
+  if ((p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) &&
+      (int64_t)BH * p->Lk + (int64_t)p->H * p->clip_k > ((int64_t)1 << 31))
+    return fail(RELATTN_ERR_UNSUPPORTED, "B*H*Lk too large for the row-constant pass");
   size_t off = 0;
-  P->off_part_o = P->off_part_ml = P->off_colc = 0;
+  P->off_part_o = P->off_part_ml = P->off_colc = P->off_colc2 = 0;
   if (splits > 1) {
     P->off_part_o = off;
     off = align256(off + (size_t)splits * BH * p->Lq * p->d * sizeof(float));
     P->off_part_ml = off;
     off = align256(off + (size_t)splits * BH * p->Lq * 2 * sizeof(float));
   }
-  if (p->kind == RELATTN_DEBERTA) {
+  if (p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) {
+    // per-key constants, 8 bytes per (head, key)
     P->off_colc = off;
     off = align256(off + (size_t)BH * p->Lk * 8);
+  }
+  if (p->kind == RELATTN_TXL) {
+    // per-distance constants v.E[r], 8 bytes per (head, encoding row)
+    P->off_colc2 = off;
+    off = align256(off + (size_t)p->H * p->clip_k * 8);
   }
   P->ws_bytes = off;
   return RELATTN_OK;
@@ -343,11 +354,35 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
     for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.t5.nthr ? P.t5.thr[m] : INT32_MAX;
   }
   hipError_t e = hipSuccess;
-  if (p->kind == RELATTN_DEBERTA) {
+  if (p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) {
+    const size_t esz = P.bf ? 2 : 4;
+    const char* t2 = reinterpret_cast<const char*>(p->table2);
+    ColcArgs ca;
+    std::memset(&ca, 0, sizeof ca);
     a.colc = ws + P.off_colc;
-    ColcArgs ca{k, p->table2, ws + P.off_colc, p->B * p->H, p->H, p->Lk, p->clip_k};
+    // rows of K: key j of head bh at k + (bh * Lk + j) * d
+    ColcJob& kj = ca.job[0];
+    kj.x = k; kj.out = ws + P.off_colc;
+    kj.x_sg = p->Lk; kj.x_sr = 1; kj.G = p->B * p->H; kj.R = p->Lk; kj.H = p->H;
+    if (p->kind == RELATTN_DEBERTA) {
+      // k_j.Qr[0][h] and k_j.Qr[2k-1][h] (Qr [2k, H, d])
+      kj.a0 = t2;
+      kj.a1 = t2 + (size_t)(2 * p->clip_k - 1) * p->H * p->d * esz;
+      ca.njobs = 1;
+    } else {
+      // u_h.k_j (table2 row 0 = u [H, d]) and v_h.E[r, h] (table2 row 1 = v;
+      // E [clip_k, H, d]: row r of head h at E + (r * H + h) * d)
+      kj.a0 = t2;
+      kj.a1 = nullptr;
+      ColcJob& ej = ca.job[1];
+      ej.x = p->table; ej.a0 = t2 + (size_t)p->H * p->d * esz; ej.a1 = nullptr;
+      ej.out = ws + P.off_colc2;
+      ej.x_sg = 1; ej.x_sr = p->H; ej.G = p->H; ej.R = p->clip_k; ej.H = p->H;
+      ca.njobs = 2;
+      a.colc2 = ws + P.off_colc2;
+    }
     e = launch_colc(P.bf, p->d, ca, st);
-    if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "colc launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "row-constant launch: %s", hipGetErrorString(e));
   }
   e = launch_fwd(p->kind, P.bf, p->d, P.var, a, P.grid, P.lds, st);
   if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));

@@ -37,7 +37,9 @@ struct FwdArgs {
   const int32_t *kv_valid_len;
   float *part_o;   // split-KV partial outputs  [n_splits][B*H][Lq][d]
   float *part_ml;  // split-KV row stats        [n_splits][B*H][Lq][2] (log2 max, sum)
-  const void *colc; // DeBERTa per-key constants [B*H][Lk] x 8 bytes (relattn_colc_kernel)
+  const void *colc; // per-key constants [B*H][Lk] x 8 bytes (relattn_colc_kernel):
+                    // DeBERTa k_j.Qr[0], k_j.Qr[2k-1]; Transformer-XL u.k_j
+  const void *colc2; // Transformer-XL per-distance constants v.E[r] [H][clip_k] x 8 bytes
   float *lse;       // [B*H][Lq] row log-sum-exp (natural log) or NULL
   int32_t B, H, Lq, Lk;
   int32_t q_pos_offset;  // query row 0 minus key row 0 (absolute positions; may be < 0)
@@ -65,10 +67,21 @@ struct IndexArgs {
   int32_t t5_thr[kT5MaxThr];  // entries from t5_nthr on hold INT32_MAX
 };
 
+// One job of relattn_colc_kernel: for g < G, r < R, entry g*R + r of `out`
+// holds (x_gr . a0_h, x_gr . a1_h) in float32 (8 bytes: a bf16 hi + lo pair
+// per constant for bf16 inputs, the float pair for float32), where
+// x_gr = x + (g * x_sg + r * x_sr) * d, h = g % H, a0_h = a0 + h * d,
+// a1_h = a1 + h * d (a1 may be NULL: the second constant is 0).
+struct ColcJob {
+  const void *x, *a0, *a1;
+  void *out;
+  int64_t x_sg, x_sr;
+  int32_t G, R, H;
+};
+
 struct ColcArgs {
-  const void *k, *qr;
-  void *colc;
-  int32_t BH, H, Lk, clip_k;
+  ColcJob job[2];
+  int32_t njobs;  // 1 or 2
 };
 
 struct CombineArgs {

@@ -484,24 +484,6 @@ __device__ __forceinline__ float ref_offset(float cb, float m_ref) {
 // constants come from relattn_colc_kernel (float32 dot products) and enter
 // the score accumulator through one MFMA: A holds the key's constants (as
 // bfloat16 hi + lo pairs, or float32), B selects the side for every query.
-// a + b elementwise, rounded to the fragment's element type
-template <int D>
-__device__ __forceinline__ TableFrag<true, D> frag_add(const TableFrag<true, D>& x, const TableFrag<true, D>& y) {
-  TableFrag<true, D> r;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[t][e] = (bf16)((float)x.v[t][e] + (float)y.v[t][e]);
-  return r;
-}
-template <int D>
-__device__ __forceinline__ TableFrag<false, D> frag_add(const TableFrag<false, D>& x, const TableFrag<false, D>& y) {
-  TableFrag<false, D> r;
-#pragma unroll
-  for (int t = 0; t < D / 2; ++t) r.v[t] = x.v[t] + y.v[t];
-  return r;
-}
-
 template <bool BF>
 struct KeyConst;
 template <>
@@ -530,15 +512,19 @@ struct KeyConst<false> {
   __device__ __forceinline__ void set(float c0, float c1, int hh) { v = hh == 0 ? c0 : c1; }
 };
 
+// c + (the side's constant of row lq) in every column; a row is a key of the
+// score block (DeBERTa, Transformer-XL u.k_j, ALiBi) or a distance of a band
+// block (Transformer-XL v.E[r])
 template <bool BF>
-__device__ __forceinline__ f32x16 mma_keyconst(const KeyConst<BF>& kc, int side, int hh) {
+__device__ __forceinline__ f32x16 mma_keyconst(const KeyConst<BF>& kc, int side, int hh,
+                                               f32x16 c = f32x16{}) {
   if constexpr (BF) {
     const bf16 one = (bf16)1.f, z = (bf16)0.f;
     bf16x8 sel = {};
     if (hh == 0) sel = side == 0 ? bf16x8{one, one, z, z, z, z, z, z} : bf16x8{z, z, one, one, z, z, z, z};
-    return mma_bf16(kc.v, sel, f32x16{});
+    return mma_bf16(kc.v, sel, c);
   } else {
-    return mma_f32(kc.v, hh == side ? 1.f : 0.f, f32x16{});
+    return mma_f32(kc.v, hh == side ? 1.f : 0.f, c);
   }
 }
 
@@ -796,22 +782,6 @@ void relattn_fwd_kernel(FwdArgs a) {
     alibi_s = reinterpret_cast<const float*>(a.table)[h] / a.scale;
     alibi_kc.set(-alibi_s * (float)lq, alibi_s * (float)lq, hh);
   }
-  // Transformer-XL: the query plus the global content bias u (against the
-  // content keys) and plus the global position bias v (against the
-  // relative encodings), each rounded to the input type
-  QFrag qv[KIND == 4 ? QB : 1];
-  if constexpr (KIND == 4) {
-    const T* uv = reinterpret_cast<const T*>(a.table2);
-    QFrag uf, vf;
-    uf.load(uv + (size_t)h * D, hh);
-    vf.load(uv + ((size_t)a.H + h) * D, hh);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      qv[qb] = frag_add<D>(qf[qb], vf);
-      qf[qb] = frag_add<D>(qf[qb], uf);
-    }
-  }
-
   const int kv_lim = max(0, min(a.Lk, kv_valid));
   const int kv_end = min(kv_lim, causal_end);
   const int n_kt = kv_end > 0 ? (kv_end + kBK - 1) / kBK : 0;
@@ -1200,11 +1170,24 @@ void relattn_fwd_kernel(FwdArgs a) {
         else if (omin >= 0) deb_side[qb] = 1;  // every key at or after every query
       }
     }
-    // DeBERTa: the per-key constants of the tile's keys (for clipped blocks)
-    KeyConst<BF> kc[KIND == 2 ? NKB : 1];
-    if constexpr (KIND == 2) {
+    // per-key constants of the tile's keys: DeBERTa k_j.Qr[0] / k_j.Qr[2k-1]
+    // (clipped blocks), Transformer-XL u.k_j
+    KeyConst<BF> kc[(KIND == 2 || KIND == 4) ? NKB : 1];
+    if constexpr (KIND == 2 || KIND == 4) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kc[kb].load(a.colc, (size_t)bh * a.Lk, min(k0 + 32 * kb + lq, a.Lk - 1), hh);
+    }
+    // Transformer-XL: v.E[r] of the band rows of the tile's blocks.  Block kb
+    // of one query block reads the distance rows T0 + 32 tb + m, T0 = T0t -
+    // 32 kb (tb = 0, 1; m = lane): entry t = 1 - kb + tb holds rows T0t +
+    // 32 (t - 1) + m (hidden negative distances read row 0)
+    KeyConst<BF> venc[KIND == 4 ? NKB + 1 : 1];
+    if constexpr (KIND == 4) {
+      static_assert(QB == 1, "Transformer-XL runs one query block per wave");
+      const int T0t = pw_min - k0 - 31;
+#pragma unroll
+      for (int t = 0; t <= NKB; ++t)
+        venc[t].load(a.colc2, (size_t)h * ck, min(max(T0t + 32 * (t - 1) + lq, 0), ck - 1), hh);
     }
     // exponent offsets c*b - m_ref of the tile's blocks
     float off[QB];
@@ -1298,6 +1281,11 @@ void relattn_fwd_kernel(FwdArgs a) {
           float* band = relf + wave * L.deb_wave_floats;
           const T* enc = reinterpret_cast<const T*>(a.table);
           const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
+          // half tb: v.E[T0 + 32 tb + m] (the position bias, a per-row
+          // constant of the band) + q.E[T0 + 32 tb + m]
+          auto band_half = [&](const int tb, const TableFrag<BF, D>& ef) -> f32x16 {
+            return mma_frag<BF, D>(ef, qf[qb], mma_keyconst<BF>(venc[1 - kb + tb], 0, hh));
+          };
           f32x16 half[2];
           if constexpr (TXL_CARRY) {
             // the previous block's first half is this block's second half
@@ -1305,14 +1293,14 @@ void relattn_fwd_kernel(FwdArgs a) {
             {
               TableFrag<BF, D> ef;
               ef.load_lds(ring + ring_slot(T0 - ring_c0) * 128, ko.k);
-              half[0] = mma_frag0<BF, D>(ef, qv[qb]);
+              half[0] = band_half(0, ef);
             }
             if (carried) {
               half[1] = txl_half[0];
             } else {
               TableFrag<BF, D> ef;
               ef.load_lds(ring + ring_slot(T0 + 32 - ring_c0) * 128, ko.k);
-              half[1] = mma_frag0<BF, D>(ef, qv[qb]);
+              half[1] = band_half(1, ef);
             }
             txl_half[0] = half[0];
             txl_t0 = T0;
@@ -1327,7 +1315,7 @@ void relattn_fwd_kernel(FwdArgs a) {
               }
             }
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) half[tb] = mma_frag0<BF, D>(ef[tb], qv[qb]);
+            for (int tb = 0; tb < 2; ++tb) half[tb] = band_half(tb, ef[tb]);
           }
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
@@ -1346,7 +1334,8 @@ void relattn_fwd_kernel(FwdArgs a) {
             for (int i = 0; i < 16; ++i) init[i] = crow[-acc_row(i, hh)];
           }
           wave_lds_fence();  // the next block overwrites the tile
-          s = mma_frag<BF, D>(kf, qf[qb], init);
+          // + u.k_j (the content bias, a per-key constant) + q.k_j
+          s = mma_frag<BF, D>(kf, qf[qb], mma_keyconst<BF>(kc[kb], 0, hh, init));
         } else {
           const int side = CLS == 0 ? deb_side[qb] : deb_block_side(qb);
           if (side >= 0) {
@@ -1867,42 +1856,56 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
   }
 }
 
-// DeBERTa per-key constants: k_j.Qr[0][h] and k_j.Qr[2k-1][h] in float32, for
-// blocks whose offsets are all clipped (key far before / far after the
-// query).  bfloat16 inputs store each as hi + lo bfloat16 ({hi0, lo0, hi1,
-// lo1} per key); float32 inputs store the pair.  Reads K once.
+// Row constants in float32 for the score terms that reduce to one value per
+// key or per relative distance:
+//   DeBERTa  k_j.Qr[0][h] and k_j.Qr[2k-1][h] (the position-to-content term
+//            of blocks whose offsets are all clipped, [DRPE]);
+//   TXL      u_h.k_j per key and v_h.E[r, h] per distance r ([RPE]
+//            Transformer-XL: the global content and position biases).
+// bfloat16 inputs store each constant as a bf16 hi + lo pair ({hi0, lo0, hi1,
+// lo1} per entry); float32 inputs store the float pair.  One thread per
+// entry; the entries of job 0 come first, then those of job 1.
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
   using T = typename std::conditional<BF, bf16, float>::type;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)a.BH * a.Lk) return;
-  const int bh = (int)(idx / a.Lk);
-  const int h = bh % a.H;
-  const T* kr = reinterpret_cast<const T*>(a.k) + idx * D;
-  const T* q0 = reinterpret_cast<const T*>(a.qr) + (size_t)h * D;
-  const T* q1 = reinterpret_cast<const T*>(a.qr) + ((size_t)(2 * a.clip_k - 1) * a.H + h) * D;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n0 = (int64_t)a.job[0].G * a.job[0].R;
+  int jb = 0;
+  if (idx >= n0) {
+    if (a.njobs < 2) return;
+    idx -= n0;
+    jb = 1;
+  }
+  const ColcJob& j = a.job[jb];
+  if (idx >= (int64_t)j.G * j.R) return;
+  const int g = (int)(idx / j.R), r = (int)(idx - (int64_t)g * j.R);
+  const int h = g % j.H;
+  const T* x = reinterpret_cast<const T*>(j.x) + ((int64_t)g * j.x_sg + (int64_t)r * j.x_sr) * D;
+  const T* v0 = reinterpret_cast<const T*>(j.a0) + (size_t)h * D;
+  const T* v1 = j.a1 ? reinterpret_cast<const T*>(j.a1) + (size_t)h * D : nullptr;
   float s0 = 0.f, s1 = 0.f;
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte load
 #pragma unroll
   for (int t = 0; t < D / EPV; ++t) {
-    const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + EPV * t);
-    const f32x4 ax = *reinterpret_cast<const f32x4*>(q0 + EPV * t);
-    const f32x4 bx = *reinterpret_cast<const f32x4*>(q1 + EPV * t);
+    const f32x4 kx = *reinterpret_cast<const f32x4*>(x + EPV * t);
+    const f32x4 ax = *reinterpret_cast<const f32x4*>(v0 + EPV * t);
     const T* ke = reinterpret_cast<const T*>(&kx);
     const T* ae = reinterpret_cast<const T*>(&ax);
-    const T* be = reinterpret_cast<const T*>(&bx);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      s0 = fmaf((float)ke[e], (float)ae[e], s0);
-      s1 = fmaf((float)ke[e], (float)be[e], s1);
+    for (int e = 0; e < EPV; ++e) s0 = fmaf((float)ke[e], (float)ae[e], s0);
+    if (v1) {
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(v1 + EPV * t);
+      const T* be = reinterpret_cast<const T*>(&bx);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) s1 = fmaf((float)ke[e], (float)be[e], s1);
     }
   }
   if constexpr (BF) {
     const bf16 h0 = (bf16)s0, h1 = (bf16)s1;
     const bf16x4 y = {h0, (bf16)(s0 - (float)h0), h1, (bf16)(s1 - (float)h1)};
-    reinterpret_cast<bf16x4*>(a.colc)[idx] = y;
+    reinterpret_cast<bf16x4*>(j.out)[idx] = y;
   } else {
-    reinterpret_cast<f32x2*>(a.colc)[idx] = f32x2{s0, s1};
+    reinterpret_cast<f32x2*>(j.out)[idx] = f32x2{s0, s1};
   }
 }
 
@@ -1966,7 +1969,9 @@ hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) 
 }
 
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st) {
-  const int64_t threads = (int64_t)a.BH * a.Lk;
+  int64_t threads = 0;
+  for (int jb = 0; jb < a.njobs; ++jb) threads += (int64_t)a.job[jb].G * a.job[jb].R;
+  if (threads == 0) return hipSuccess;
   const int grid = (int)((threads + 255) / 256);
   if (bf && d == 128) hipLaunchKernelGGL((relattn_colc_kernel<true, 128>), dim3(grid), dim3(256), 0, st, a);
   else if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
