@@ -308,19 +308,21 @@ relattn_status relattn_workspace_bytes(const relattn_params* p, size_t* bytes) {
   return ok();
 }
 
-relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k, const void* v,
-                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  Plan P;
-  relattn_status s = plan_problem(p, &P);
-  if (s != RELATTN_OK) return s;
+}  // extern "C"
+
+namespace {
+
+relattn_status check_tensors(const void* q, const void* k, const void* v, const void* out) {
   if (!q || !k || !v || !out) return fail(RELATTN_ERR_INVALID, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(RELATTN_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
-  if (P.ws_bytes > 0 && (!workspace || workspace_bytes < P.ws_bytes))
-    return fail(RELATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", P.ws_bytes,
-                workspace_bytes, workspace ? "" : ", NULL");
-  if (workspace && !aligned16(workspace)) return fail(RELATTN_ERR_INVALID, "workspace must be 16-byte aligned");
+  return RELATTN_OK;
+}
 
+// Enqueue the kernels of one planned call; `workspace` holds at least
+// P.ws_bytes bytes (checked by the caller).
+relattn_status enqueue(const relattn_params* p, const Plan& P, const void* q, const void* k,
+                       const void* v, void* out, void* workspace, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   FwdArgs a;
@@ -392,6 +394,24 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
     if (e != hipSuccess) return fail(RELATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k, const void* v,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  relattn_status s = plan_problem(p, &P);
+  if (s != RELATTN_OK) return s;
+  s = check_tensors(q, k, v, out);
+  if (s != RELATTN_OK) return s;
+  if (P.ws_bytes > 0 && (!workspace || workspace_bytes < P.ws_bytes))
+    return fail(RELATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", P.ws_bytes,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (workspace && !aligned16(workspace)) return fail(RELATTN_ERR_INVALID, "workspace must be 16-byte aligned");
+  return enqueue(p, P, q, k, v, out, workspace, stream);
 }
 
 relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, const int32_t* k_pos,
