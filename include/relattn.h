@@ -162,6 +162,26 @@ relattn_status relattn_fwd(const relattn_params *p, const void *q, const void *k
                            const void *v, void *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * Fused forward that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, arguments (minus the
+ * workspace) and errors as relattn_fwd.  The workspace is a fixed array of
+ * RELATTN_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * until the process ends; a problem whose relattn_workspace_bytes() exceeds
+ * it returns RELATTN_ERR_WORKSPACE and launches nothing.  The array's device
+ * address is looked up once per device, on the first call made with that
+ * device current (the stream must belong to the current device).  Every
+ * call on one GPU shares that GPU's array and it keeps the last call's
+ * contents: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  No part of the array
+ * needs to start at zero.  The call itself allocates nothing (no hipMalloc,
+ * no allocating library routine).
+ */
+#define RELATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+relattn_status relattn_fwd_noalloc(const relattn_params *p, const void *q, const void *k,
+                                   const void *v, void *out, void *stream);
+
 /* Bytes of device workspace relattn_fwd needs for this problem: the split-KV
  * partial results of decode-like shapes; for DEBERTA the per-key
  * position-to-content constants of clipped blocks (8 bytes per key and

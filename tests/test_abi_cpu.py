@@ -281,3 +281,25 @@ def test_binding_rel_index_checks():
         ra.relattn_rel_index("t5", qp, torch.zeros(8, dtype=torch.int64))
     with pytest.raises(ValueError, match="GPU tensor"):
         ra.relattn_rel_index("t5", qp, qp.clone())
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    # DeBERTa's per-key constants of 64 x 16 heads x 4096 keys take 32 MiB,
+    # twice the fixed scratch: refused before any HIP call, with the reason
+    p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=512, B=64, H=16, Lq=4096,
+                Lk=4096)
+    need = ra.relattn_workspace_bytes(p)
+    assert need > ra.binding.NOALLOC_SCRATCH_BYTES
+    st = lib.relattn_fwd_noalloc(ctypes.byref(p), 0x10000, 0x10000, 0x10000, 0x10000, None)
+    assert st == 3
+    msg = lib.relattn_last_error().decode()
+    assert "scratch" in msg and str(need) in msg
+    # and the usual argument checks come first
+    assert lib.relattn_fwd_noalloc(ctypes.byref(p), None, None, None, None, None) == 1
+    assert lib.relattn_fwd_noalloc(None, None, None, None, None, None) == 1
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define RELATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ra.binding.NOALLOC_SCRATCH_BYTES

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     load_library,
     make_params,
     relattn_fwd,
+    relattn_fwd_noalloc,
     relattn_rel_index,
     relattn_t5_thresholds,
     relattn_workspace_bytes,

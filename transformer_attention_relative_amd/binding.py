@@ -45,9 +45,11 @@ class relattn_params(ctypes.Structure):
     ]
 
 
-EXPORTS = ("relattn_fwd", "relattn_workspace_bytes", "relattn_rel_index",
+EXPORTS = ("relattn_fwd", "relattn_fwd_noalloc", "relattn_workspace_bytes", "relattn_rel_index",
            "relattn_t5_thresholds", "relattn_status_str", "relattn_last_error",
            "relattn_abi_version")
+# bytes of the fixed device scratch behind relattn_fwd_noalloc
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 _lock = threading.Lock()
@@ -68,6 +70,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lib.relattn_fwd.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         lib.relattn_fwd.restype = i32
+        lib.relattn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp]
+        lib.relattn_fwd_noalloc.restype = i32
         lib.relattn_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
         lib.relattn_workspace_bytes.restype = i32
         lib.relattn_rel_index.argtypes = [P, vp, vp, i64, i32, vp, vp]
@@ -182,6 +186,42 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
     before the library is called.
     """
     import torch
+    lib, p, out = _checked_call(q, k, v, kind, table, table2, num_buckets, max_distance,
+                                bidirectional, clip_k, q_pos_offset, k_pos_offset, causal,
+                                kv_valid_len, scale, out, workspace, lse)
+    nbytes = relattn_workspace_bytes(p)
+    if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if nbytes else None
+    ws_len = workspace.numel() * workspace.element_size() if (nbytes and workspace is not None) else 0
+    _check(lib, lib.relattn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), ws_ptr, ws_len, _stream_handle(q.device)))
+    return out
+
+
+def relattn_fwd_noalloc(q, k, v, kind: str, table=None, table2=None, *, out, num_buckets: int = 32,
+                        max_distance: int = 128, bidirectional: bool = True, clip_k: int = 0,
+                        q_pos_offset: int = 0, k_pos_offset: int = 0, causal: bool = False,
+                        kv_valid_len=None, scale: float = 0.0, lse=None):
+    """relattn_fwd without a workspace: the library's fixed device scratch
+    (one per GPU) holds it, and nothing is allocated; ``out`` must be given.
+    Calls that overlap in time on one GPU share that scratch and must be
+    ordered by the caller (include/relattn.h)."""
+    if out is None:
+        raise ValueError("relattn_fwd_noalloc writes into a given `out`")
+    lib, p, out = _checked_call(q, k, v, kind, table, table2, num_buckets, max_distance,
+                                bidirectional, clip_k, q_pos_offset, k_pos_offset, causal,
+                                kv_valid_len, scale, out, None, lse)
+    _check(lib, lib.relattn_fwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), out.data_ptr(), _stream_handle(q.device)))
+    return out
+
+
+def _checked_call(q, k, v, kind, table, table2, num_buckets, max_distance, bidirectional,
+                  clip_k, q_pos_offset, k_pos_offset, causal, kv_valid_len, scale, out,
+                  workspace, lse):
+    """Check every tensor, load the library; return (lib, params, out)."""
+    import torch
     if kind not in KINDS:
         raise ValueError(f"unknown kind {kind!r}")
     if q.dtype == torch.float32:
@@ -228,14 +268,7 @@ def relattn_fwd(q, k, v, kind: str, table=None, table2=None, *, num_buckets: int
                     scale=scale, lse=lse)
     if out is None:
         out = torch.empty_like(q)
-    nbytes = relattn_workspace_bytes(p)
-    if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    ws_ptr = _ptr(workspace) if nbytes else None
-    ws_len = workspace.numel() * workspace.element_size() if (nbytes and workspace is not None) else 0
-    _check(lib, lib.relattn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                out.data_ptr(), ws_ptr, ws_len, _stream_handle(q.device)))
-    return out
+    return lib, p, out
 
 
 def relattn_rel_index(kind: str, q_pos, k_pos, which: int = 0, *, num_buckets: int = 32,

@@ -19,9 +19,13 @@ bool fwd_variant_built(int kind, bool bf, int d, Variant v);
 hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st);
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st);
 hipError_t launch_index(const IndexArgs& a, hipStream_t st);
+hipError_t scratch_address(void** ptr);
 }  // namespace relattn
 
 using namespace relattn;
+
+static_assert(kScratchBytes == RELATTN_NOALLOC_SCRATCH_BYTES,
+              "the device scratch array and the header disagree on its size");
 
 namespace {
 
@@ -412,6 +416,27 @@ relattn_status relattn_fwd(const relattn_params* p, const void* q, const void* k
                 workspace_bytes, workspace ? "" : ", NULL");
   if (workspace && !aligned16(workspace)) return fail(RELATTN_ERR_INVALID, "workspace must be 16-byte aligned");
   return enqueue(p, P, q, k, v, out, workspace, stream);
+}
+
+relattn_status relattn_fwd_noalloc(const relattn_params* p, const void* q, const void* k,
+                                   const void* v, void* out, void* stream) {
+  Plan P;
+  relattn_status s = plan_problem(p, &P);
+  if (s != RELATTN_OK) return s;
+  s = check_tensors(q, k, v, out);
+  if (s != RELATTN_OK) return s;
+  if (P.ws_bytes > kScratchBytes)
+    return fail(RELATTN_ERR_WORKSPACE,
+                "problem needs %zu bytes of workspace; the fixed device scratch of "
+                "relattn_fwd_noalloc holds %zu (use relattn_fwd with a workspace)",
+                P.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (P.ws_bytes > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess)
+      return fail(RELATTN_ERR_HIP, "device scratch address: %s", hipGetErrorString(e));
+  }
+  return enqueue(p, P, q, k, v, out, ws, stream);
 }
 
 relattn_status relattn_rel_index(const relattn_params* p, const int32_t* q_pos, const int32_t* k_pos,

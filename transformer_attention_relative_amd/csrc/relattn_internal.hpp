@@ -28,6 +28,8 @@ constexpr int kNumXcd = 8;        // MI355X: 8 XCDs of 32 CUs
 constexpr int kCuPerXcd = 32;
 constexpr int kMaxSortSeqs = 64;  // sequences a workgroup orders by valid length (one wave)
 constexpr int kLdsPerCU = 160 * 1024;
+// device scratch of relattn_fwd_noalloc (one array per GPU, fixed size)
+constexpr size_t kScratchBytes = size_t(16) << 20;
 
 // Kernel argument block (passed by value).
 struct FwdArgs {

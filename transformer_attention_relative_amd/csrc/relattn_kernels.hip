@@ -41,6 +41,7 @@
 //     a per-key constant ([DRPE]: every offset beyond +-k uses a boundary row).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "relattn_internal.hpp"
@@ -1912,6 +1913,37 @@ __global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
 // ----------------------------------------------------------------------------
 // Host-side launch helpers (called from relattn_api.cpp)
 // ----------------------------------------------------------------------------
+
+// Device scratch of relattn_fwd_noalloc: the workspace (split-KV partials,
+// row constants) of callers that cannot allocate.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` is a
+// host-side stand-in for the symbol, not a device address: its address on a
+// device comes from hipGetSymbolAddress with that device current, kept per
+// device, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 template <int KIND, bool BF, int D, int QB, int NW>
 static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t st) {
