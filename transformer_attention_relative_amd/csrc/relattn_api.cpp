@@ -246,10 +246,11 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     P->cu_slots = std::max(1, std::min(by_regs, by_lds));
   }
 
-  // the row-constant pre-pass runs one thread per (head, key) and per
-  // (head, encoding row)
+  // the row-constant pre-pass runs one lane per 16-byte chunk of every
+  // (head, key) row and every (head, encoding row)
   if ((p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) &&
-      (int64_t)BH * p->Lk + (int64_t)p->H * p->clip_k > ((int64_t)1 << 31))
+      ((int64_t)BH * p->Lk + (p->kind == RELATTN_TXL ? (int64_t)p->H * p->clip_k : 0)) *
+              (p->d * (P->bf ? 2 : 4) / 16) >= ((int64_t)1 << 31))
     return fail(RELATTN_ERR_UNSUPPORTED, "B*H*Lk too large for the row-constant pass");
   size_t off = 0;
   P->off_part_o = P->off_part_ml = P->off_colc = P->off_colc2 = 0;

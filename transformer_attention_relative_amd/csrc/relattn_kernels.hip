@@ -976,6 +976,13 @@ void relattn_fwd_kernel(FwdArgs a) {
   constexpr bool TXL_CARRY = KIND == 4 && KR_RING;
   f32x16 txl_half[1];
   int txl_t0 = -(1 << 30);  // no block yet
+  // DeBERTa (same kernel): the first half of the Qr rows of the wave's next
+  // key block (distances T0 - 32 ..), requested right after this block's
+  // band products, so its latency hides behind this block's softmax and
+  // P V; tagged with the block's T0
+  constexpr bool QR_NEXT = KIND == 2 && KR_RING;
+  TableFrag<BF, D> qr_next;
+  int qr_t0 = -(1 << 30);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -1352,7 +1359,16 @@ void relattn_fwd_kernel(FwdArgs a) {
             const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
             // the four table fragments of the block's two bands are requested
             // together, so their L2 latencies overlap instead of adding up
-            TableFrag<BF, D> af[2], bfr[2];
+            // Qr rows delta(-(T0 + 32 nb + lane)) (the position-to-content
+            // band's A operand); the first half may have been requested by
+            // the previous block
+            TableFrag<BF, D> bfr[2];
+            if (QR_NEXT && qr_t0 == T0) bfr[0] = qr_next;
+            else bfr[0].load(qr + ((size_t)deberta_delta_dev(-(T0 + lq), ck) * a.H + h) * D, hh);
+            bfr[1].load(qr + ((size_t)deberta_delta_dev(-(T0 + 32 + lq), ck) * a.H + h) * D, hh);
+            // content-to-position: rows Kr[delta(T0 + m)], columns = queries,
+            // stored [query][m]
+            TableFrag<BF, D> af[2];
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
               if constexpr (KR_RING) {
@@ -1362,11 +1378,6 @@ void relattn_fwd_kernel(FwdArgs a) {
                 af[tb].load(kr + ((size_t)deberta_delta_dev(T0 + 32 * tb + lq, ck) * a.H + h) * D, hh);
               }
             }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              bfr[nb].load(qr + ((size_t)deberta_delta_dev(-(T0 + 32 * nb + lq), ck) * a.H + h) * D, hh);
-            // content-to-position: rows Kr[delta(T0 + m)], columns = queries,
-            // stored [query][m]
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
               const f32x16 acc = mma_frag0<BF, D>(af[tb], qf[qb]);
@@ -1385,16 +1396,27 @@ void relattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
               for (int i = 0; i < 16; ++i) cg[i] = crow[-acc_row(i, hh)];
             }
-            // position-to-content: rows = keys, columns n <-> query - key =
-            // T0 + n, Qr row delta(key - query); stored [key][n] over the
-            // same tile (the reads above precede these writes in the wave's
-            // LDS order): every address is a lane base plus a constant
+            // position-to-content: rows n <-> query - key = T0 + n (Qr row
+            // delta(key - query), the A operand), columns = keys (the K
+            // fragment as the B operand); register 4g + e of a lane holds n =
+            // 32 nb + 8g + 4hh + e of its key, so the tile [key][n] takes one
+            // 16-byte store per four registers.  The tile is the one the
+            // reads above used (they precede these writes in the wave's LDS
+            // order).
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-              const f32x16 acc = mma_frag0<BF, D>(kf, bfr[nb]);
-              float* dst = band + 32 * nb + lq;
+              const f32x16 acc = mma_frag0<BF, D>(bfr[nb], kf);
+              float* dst = band + lq * kCbandStride + 32 * nb + 4 * hh;
 #pragma unroll
-              for (int i = 0; i < 16; ++i) dst[acc_row(i, hh) * kCbandStride] = acc[i];
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 x = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+                *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
+              }
+            }
+            if constexpr (QR_NEXT) {
+              // the next key block's first half: distances T0 - 32 + lane
+              qr_next.load(qr + ((size_t)deberta_delta_dev(-(T0 - 32 + lq), ck) * a.H + h) * D, hh);
+              qr_t0 = T0 - 32;
             }
             wave_lds_fence();
             // key j0 + jl of query row lq sits at n = lq - jl + 31
@@ -1464,7 +1486,9 @@ void relattn_fwd_kernel(FwdArgs a) {
       // One query block per wave leaves registers to spare: the V^T
       // fragments of the step are read before the softmax, so their LDS
       // latency hides behind it instead of sitting between it and P V.
-      constexpr bool EARLY_V = BF && QB == 1 && D <= 64;
+      // (not in DeBERTa's eight-wave kernel, which spends these registers on
+      // the requested Qr rows)
+      constexpr bool EARLY_V = BF && QB == 1 && D <= 64 && !QR_NEXT;
       bf16x8 vpre[EARLY_V ? 2 : 1][EARLY_V ? NDB : 1];
       if constexpr (EARLY_V) {
 #pragma unroll
@@ -1717,6 +1741,13 @@ void relattn_fwd_kernel(FwdArgs a) {
   while (r < n_my) {
     const int cls = tile_class(r);
     const int ln = opaque_lane();
+    if constexpr (QR_NEXT) {
+      if (cls != 2) {
+        // no near block follows within this run: drop the requested Qr rows
+        qr_t0 = -(1 << 30);
+        qr_next.zero();
+      }
+    }
     if (cls == 0) {
       do { run_tile(C0{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 0);
     } else if (cls == 1) {
@@ -1864,43 +1895,57 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
 //   TXL      u_h.k_j per key and v_h.E[r, h] per distance r ([RPE]
 //            Transformer-XL: the global content and position biases).
 // bfloat16 inputs store each constant as a bf16 hi + lo pair ({hi0, lo0, hi1,
-// lo1} per entry); float32 inputs store the float pair.  One thread per
-// entry; the entries of job 0 come first, then those of job 1.
+// lo1} per entry); float32 inputs store the float pair.  A row of d elements
+// is CPR 16-byte chunks; CPR consecutive lanes take one row (lane c its chunk
+// c), so a wave reads 64 / CPR whole rows, one contiguous run per load when
+// the rows are adjacent, and the partial dot products meet by lane exchanges.
+// The entries of job 0 come first, then those of job 1.
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
   using T = typename std::conditional<BF, bf16, float>::type;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / EPV;         // chunks per row (4 .. 16)
+  static_assert(CPR >= 2 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "chunks per row");
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int c = (int)(t % CPR);
+  int64_t idx = t / CPR;               // entry (row) of this group of lanes
   const int64_t n0 = (int64_t)a.job[0].G * a.job[0].R;
+  const int64_t n1 = a.njobs > 1 ? (int64_t)a.job[1].G * a.job[1].R : 0;
+  // every lane of a row group stays for the exchanges; a group past the last
+  // entry computes nothing and stores nothing
+  const bool live = idx < n0 + n1;
   int jb = 0;
   if (idx >= n0) {
-    if (a.njobs < 2) return;
     idx -= n0;
     jb = 1;
   }
-  const ColcJob& j = a.job[jb];
-  if (idx >= (int64_t)j.G * j.R) return;
-  const int g = (int)(idx / j.R), r = (int)(idx - (int64_t)g * j.R);
-  const int h = g % j.H;
-  const T* x = reinterpret_cast<const T*>(j.x) + ((int64_t)g * j.x_sg + (int64_t)r * j.x_sr) * D;
-  const T* v0 = reinterpret_cast<const T*>(j.a0) + (size_t)h * D;
-  const T* v1 = j.a1 ? reinterpret_cast<const T*>(j.a1) + (size_t)h * D : nullptr;
   float s0 = 0.f, s1 = 0.f;
-  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte load
-#pragma unroll
-  for (int t = 0; t < D / EPV; ++t) {
-    const f32x4 kx = *reinterpret_cast<const f32x4*>(x + EPV * t);
-    const f32x4 ax = *reinterpret_cast<const f32x4*>(v0 + EPV * t);
+  const ColcJob& j = a.job[jb];
+  if (live) {
+    const int g = (int)(idx / j.R), r = (int)(idx - (int64_t)g * j.R);
+    const int h = g % j.H;
+    const T* x = reinterpret_cast<const T*>(j.x) + ((int64_t)g * j.x_sg + (int64_t)r * j.x_sr) * D + c * EPV;
+    const f32x4 kx = *reinterpret_cast<const f32x4*>(x);
+    const f32x4 ax = *reinterpret_cast<const f32x4*>(reinterpret_cast<const T*>(j.a0) + (size_t)h * D + c * EPV);
     const T* ke = reinterpret_cast<const T*>(&kx);
     const T* ae = reinterpret_cast<const T*>(&ax);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) s0 = fmaf((float)ke[e], (float)ae[e], s0);
-    if (v1) {
-      const f32x4 bx = *reinterpret_cast<const f32x4*>(v1 + EPV * t);
+    if (j.a1) {
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const T*>(j.a1) + (size_t)h * D + c * EPV);
       const T* be = reinterpret_cast<const T*>(&bx);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) s1 = fmaf((float)ke[e], (float)be[e], s1);
     }
   }
+  // sum over the CPR lanes of the row (a fixed order, so the result does not
+  // depend on the launch)
+#pragma unroll
+  for (int m = 1; m < CPR; m <<= 1) {
+    s0 += __shfl_xor(s0, m);
+    s1 += __shfl_xor(s1, m);
+  }
+  if (!live || c != 0) return;
   if constexpr (BF) {
     const bf16 h0 = (bf16)s0, h1 = (bf16)s1;
     const bf16x4 y = {h0, (bf16)(s0 - (float)h0), h1, (bf16)(s1 - (float)h1)};
@@ -2001,9 +2046,10 @@ hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) 
 }
 
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st) {
-  int64_t threads = 0;
-  for (int jb = 0; jb < a.njobs; ++jb) threads += (int64_t)a.job[jb].G * a.job[jb].R;
-  if (threads == 0) return hipSuccess;
+  int64_t rows = 0;
+  for (int jb = 0; jb < a.njobs; ++jb) rows += (int64_t)a.job[jb].G * a.job[jb].R;
+  if (rows == 0) return hipSuccess;
+  const int64_t threads = rows * (d * (bf ? 2 : 4) / 16);  // one lane per 16-byte chunk
   const int grid = (int)((threads + 255) / 256);
   if (bf && d == 128) hipLaunchKernelGGL((relattn_colc_kernel<true, 128>), dim3(grid), dim3(256), 0, st, a);
   else if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
