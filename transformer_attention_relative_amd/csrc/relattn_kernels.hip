@@ -1097,9 +1097,31 @@ void relattn_fwd_kernel(FwdArgs a) {
       } else {
         wait_vmcnt<0>();
       }
-      __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     }
     const int k0 = kt * kBK;
+    // The tile's row constants from global memory, requested before the
+    // workgroup barrier so that their latency overlaps the wait for the other
+    // waves (they are first read after it).
+    //   per-key constants of the tile's keys: DeBERTa k_j.Qr[0] / k_j.Qr[2k-1]
+    //   (clipped blocks), Transformer-XL u.k_j;
+    //   Transformer-XL v.E[r] of the band rows of the tile's blocks: block kb
+    //   of one query block reads the distance rows T0 + 32 tb + m, T0 = T0t -
+    //   32 kb (tb = 0, 1; m = lane), so entry t = 1 - kb + tb holds rows T0t +
+    //   32 (t - 1) + m (hidden negative distances read row 0)
+    KeyConst<BF> kc[(KIND == 2 || KIND == 4) ? NKB : 1];
+    KeyConst<BF> venc[KIND == 4 ? NKB + 1 : 1];
+    if constexpr ((KIND == 2 || KIND == 4) && CLS != 3) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kc[kb].load(a.colc, (size_t)bh * a.Lk, min(k0 + 32 * kb + lq, a.Lk - 1), hh);
+    }
+    if constexpr (KIND == 4 && CLS != 3) {
+      static_assert(QB == 1, "Transformer-XL runs one query block per wave");
+      const int T0t = pw_min - k0 - 31;
+#pragma unroll
+      for (int t = 0; t <= NKB; ++t)
+        venc[t].load(a.colc2, (size_t)h * ck, min(max(T0t + 32 * (t - 1) + lq, 0), ck - 1), hh);
+    }
+    if constexpr (!PAIR) __syncthreads();  // tile r landed for every wave; every wave is done with tile r-1
     // Lean tiles in bfloat16 run as a software pipeline (below); T5 with two
     // query blocks per wave or 128-wide heads keeps the step loop (the
     // pipeline's extra live registers spill there)
@@ -1177,25 +1199,6 @@ void relattn_fwd_kernel(FwdArgs a) {
         if (omax <= 0) deb_side[qb] = 0;       // every key at or before every query
         else if (omin >= 0) deb_side[qb] = 1;  // every key at or after every query
       }
-    }
-    // per-key constants of the tile's keys: DeBERTa k_j.Qr[0] / k_j.Qr[2k-1]
-    // (clipped blocks), Transformer-XL u.k_j
-    KeyConst<BF> kc[(KIND == 2 || KIND == 4) ? NKB : 1];
-    if constexpr (KIND == 2 || KIND == 4) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kc[kb].load(a.colc, (size_t)bh * a.Lk, min(k0 + 32 * kb + lq, a.Lk - 1), hh);
-    }
-    // Transformer-XL: v.E[r] of the band rows of the tile's blocks.  Block kb
-    // of one query block reads the distance rows T0 + 32 tb + m, T0 = T0t -
-    // 32 kb (tb = 0, 1; m = lane): entry t = 1 - kb + tb holds rows T0t +
-    // 32 (t - 1) + m (hidden negative distances read row 0)
-    KeyConst<BF> venc[KIND == 4 ? NKB + 1 : 1];
-    if constexpr (KIND == 4) {
-      static_assert(QB == 1, "Transformer-XL runs one query block per wave");
-      const int T0t = pw_min - k0 - 31;
-#pragma unroll
-      for (int t = 0; t <= NKB; ++t)
-        venc[t].load(a.colc2, (size_t)h * ck, min(max(T0t + 32 * (t - 1) + lq, 0), ck - 1), hh);
     }
     // exponent offsets c*b - m_ref of the tile's blocks
     float off[QB];
