@@ -256,6 +256,49 @@ def test_parity_split_kv(wl):
     check_close(got.float().numpy(), want, wl.dtype, _case_id(wl))
 
 
+# Decode-like T5 / ALiBi shapes with several query blocks run workgroups of
+# eight waves as two halves over the same 128 query rows, each half taking
+# half of the workgroup's key tiles, merged through LDS at the end: one tile
+# (the second half idles), odd tile counts (it idles for the last step),
+# causal masks with shifted positions, per-sequence valid lengths, ALiBi,
+# and the row LSE of the merged halves.
+KEY_SPLIT_CASES = [
+    Workload(name="ks", kind="t5", B=1, H=3, Lq=96, Lk=64, d=64, dtype="bf16"),
+    Workload(name="ks", kind="t5", B=1, H=2, Lq=128, Lk=5, d=64, dtype="bf16",
+             bidirectional=False, causal=True, q_pos_offset=4),
+    Workload(name="ks", kind="t5", B=2, H=2, Lq=128, Lk=197, d=32, dtype="bf16",
+             bidirectional=False, causal=True, q_pos_offset=69),
+    Workload(name="ks", kind="t5", B=1, H=2, Lq=200, Lk=450, d=64, dtype="bf16",
+             valid_len_range=(1, 450)),
+    Workload(name="ks", kind="t5", B=1, H=3, Lq=257, Lk=3000, d=64, dtype="bf16",
+             bidirectional=False, causal=True, q_pos_offset=2743),
+    Workload(name="ks", kind="t5", B=2, H=1, Lq=33, Lk=900, d=64, dtype="bf16",
+             num_buckets=64, max_distance=100, k_pos_offset=300, q_pos_offset=1000,
+             bidirectional=False, causal=True),
+    Workload(name="ks", kind="alibi", B=2, H=3, Lq=130, Lk=333, d=64, dtype="bf16",
+             causal=True, q_pos_offset=203),
+    Workload(name="ks", kind="alibi", B=1, H=1, Lq=64, Lk=5, d=64, dtype="bf16"),
+    Workload(name="ks", kind="alibi", B=1, H=4, Lq=128, Lk=2100, d=32, dtype="bf16",
+             valid_len_range=(600, 2100)),
+]
+
+
+@pytest.mark.parametrize("wl", KEY_SPLIT_CASES, ids=lambda w: _case_id(w) + f"-B{w.B}H{w.H}")
+def test_parity_key_split_halves(wl):
+    inp = make_inputs(wl, seed=25)
+    out, lse = run_gpu(wl, _to_dev(inp), lse=True)
+    want_o, want_l = oracle.relattn_forward(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), wl.kind,
+                                            _np(inp["table"]), _np(inp["table2"]),
+                                            kv_valid_len=None if inp["kv_valid_len"] is None
+                                            else inp["kv_valid_len"].numpy(),
+                                            return_lse=True, **params_of(wl))
+    check_close(out.cpu().float().numpy(), want_o, wl.dtype, _case_id(wl))
+    got_l = lse.cpu().numpy().astype(np.float64)
+    dead = np.isneginf(want_l)
+    assert np.array_equal(np.isneginf(got_l), dead)
+    assert np.abs(got_l[~dead] - want_l[~dead]).max() <= LSE_TOL[wl.dtype]
+
+
 # ----------------------------------------------------------------------------
 # 2b. key positions (a cache whose oldest keys were dropped: [RPE] "Kernels
 #     and the KV cache") and one-token decode steps ([T5B], cached decoding)

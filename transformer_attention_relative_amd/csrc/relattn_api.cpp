@@ -198,6 +198,17 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
         t2 <= kLdsPerCU / 2)
       var = Variant{4, 2};
   }
+  if ((p->kind == RELATTN_T5 || p->kind == RELATTN_ALIBI) && P->bf && p->d <= 64 &&
+      p->Lq > kBlockRows && var.qb == 1) {
+    // Decode-like shapes with several query blocks (a block of cached
+    // queries against a long key range): four-wave workgroups would leave
+    // one wave per SIMD, so each workgroup takes eight waves as two halves
+    // over the same query rows, each half running half of the key tiles
+    const int64_t wgs4 = (int64_t)BH * ((p->Lq + 4 * kBlockRows - 1) / (4 * kBlockRows));
+    int t8 = 0;
+    if (wgs4 < kNumCU && lds_for(Variant{8, 1}, &t8, &lut_n) == RELATTN_OK && t8 <= kLdsPerCU)
+      var = Variant{8, 1};
+  }
   relattn_status ls = lds_for(var, &lds_total, &lut_n);
   if (ls != RELATTN_OK) return ls;
   if (lds_total > kLdsPerCU && p->kind == RELATTN_SHAW && !P->bf) {
@@ -208,7 +219,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   }
   if (!fwd_variant_built(p->kind, P->bf, p->d, var)) return fail(RELATTN_ERR_UNSUPPORTED, "no kernel variant");
   P->var = var;
-  const int BQ = kBlockRows * var.qb * var.nw;
+  const int BQ = kBlockRows * var.qb * var.nw / key_split(p->kind, var.nw);  // query rows per workgroup
   P->n_qtiles = (p->Lq + BQ - 1) / BQ;
   const int64_t wgs = (int64_t)BH * P->n_qtiles;
   // keys visible to the last query row (causal): key index j sees rows with

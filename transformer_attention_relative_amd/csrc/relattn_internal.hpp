@@ -103,6 +103,14 @@ RELATTN_HD constexpr int num_stages(int kind, bool bf16, int d) {
   return d > 64 ? 2 : ((kind == 0 || kind == 3) ? (bf16 ? 4 : 3) : 2);
 }
 
+// Key split inside a workgroup: T5 and ALiBi workgroups of eight waves are
+// two halves of four waves over the same query rows, each running half of
+// the workgroup's key tiles with its own stage ring (decode-like shapes,
+// where four-wave workgroups leave one wave per SIMD); 1 = no split.
+RELATTN_HD constexpr int key_split(int kind, int nw) {
+  return ((kind == 0 || kind == 3) && nw == 8) ? 2 : 1;
+}
+
 // Shaw bins strictly inside the clip window (offsets -k+1 .. k-1), padded to
 // whole MFMA contraction chunks.
 RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k - 1) + 15) / 16 * 16; }
@@ -116,6 +124,8 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 
 // ---- LDS layout ------------------------------------------------------------
 // Stage s holds the K tile then the V tile of one key tile, each kBK rows of
+// d elements (with a key split, each half has its own ring of stages, half h
+// at h * stages * stage_bytes), each kBK rows of
 // d elements, row-major; 16-byte chunks are XOR-swizzled within a row
 // (chunk c of row r sits in slot c ^ (r & 7)) so that column reads of
 // consecutive rows hit different banks.  After the stages, per kind:
@@ -160,7 +170,7 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
   const int esz = bf16 ? 2 : 4;
   L.tile_bytes = kBK * d * esz;
   L.stage_bytes = 2 * L.tile_bytes;
-  L.rel_off = num_stages(kind, bf16, d) * L.stage_bytes;
+  L.rel_off = key_split(kind, nw) * num_stages(kind, bf16, d) * L.stage_bytes;
   int rel_bytes = 0;
   if (kind == 0) {
     // stride = 16 (mod 64) floats: four lanes reading the four copies at one

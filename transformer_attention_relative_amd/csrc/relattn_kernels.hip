@@ -576,12 +576,17 @@ template <int KIND, bool BF, int D, int QB, int NW>
 __global__ __launch_bounds__(64 * NW, (D > 64 && KIND != 0 && KIND != 3) ? 1 : 8 / NW)
 void relattn_fwd_kernel(FwdArgs a) {
   static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
+  // KS = 2: waves 0 .. NW/2-1 and NW/2 .. NW-1 are two halves over the same
+  // query rows, each with half of the workgroup's key tiles (key_split)
+  constexpr int KS = key_split(KIND, NW);
+  constexpr int NWQ = NW / KS;        // waves over distinct query rows
+  static_assert(KS == 1 || QB == 1, "a key split runs one query block per wave");
   using T = typename std::conditional<BF, bf16, float>::type;
   using QFrag = TableFrag<BF, D>;
   constexpr int NKB = kBK / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
   constexpr int RW = 32 * QB;         // query rows per wave
-  constexpr int BQ = RW * NW;         // query rows per workgroup
+  constexpr int BQ = RW * NWQ;        // query rows per workgroup
   constexpr int NS = num_stages(KIND, BF, D);
   // Four stages go in pairs: one wait, one barrier and two tile copies per
   // two tiles (the copies of tiles r+2 and r+3 at even r), so each copy
@@ -590,15 +595,16 @@ void relattn_fwd_kernel(FwdArgs a) {
   // ring stage of tile r (r >= 0)
   auto stage_of = [](const int r) -> int { return (int)((unsigned)r % (unsigned)NS); };
   constexpr int AHEAD = PAIR ? 2 : NS - 1;  // tiles copied before the loop
-  using Dma = TileDma<BF, D, NW>;
+  using Dma = TileDma<BF, D, NWQ>;    // the waves of one half share a tile's copies
   constexpr int ROWB = Dma::ROWB;     // bytes per K / V row
   constexpr int LPW = Dma::LPW;       // load instructions per wave per tile
-  constexpr bool EVEN_LOADS = (Dma::IPT % NW) == 0;
+  constexpr bool EVEN_LOADS = (Dma::IPT % NWQ) == 0;
   constexpr float NEG_INF = RA_NEG_INF;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const LdsLayout L = lds_layout(KIND, BF, D, QB, NW, a.clip_k, a.lut_n);
   float* relf = reinterpret_cast<float*>(smem + L.rel_off);
+  // this wave's ring of key/value stages (one per key-split half)
 
   // ---- work item -------------------------------------------------------------
   // Work items in order of decreasing work: the query-tile rank is the
@@ -637,16 +643,28 @@ void relattn_fwd_kernel(FwdArgs a) {
   // the wave index is uniform across the wave; say so, so that everything
   // derived from it (positions, tile classes) lives in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = KS == 2 ? wave / NWQ : 0;    // key-split half
+  const int wq = wave - half * NWQ;             // wave within the half
   const int lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
   const int q0 = qt * BQ;
-  const int wrow0 = q0 + wave * RW;
+  const int wrow0 = q0 + wq * RW;
   const int pw_min = a.q_pos_offset + wrow0;
   const bool wave_active = wrow0 < a.Lq;
   const int pw_max_real = a.q_pos_offset + min(wrow0 + RW, a.Lq) - 1;
   int qrow[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) qrow[qb] = wrow0 + 32 * qb + lq;
+  char* const sbase = smem + half * NS * L.stage_bytes;
+  // the part of a workgroup's key-tile range [kb, ke) this wave's half runs:
+  // the first ceil(n / 2) tiles for half 0, the rest for half 1
+  auto half_range = [&](int& kb, int& ke) {
+    if constexpr (KS == 2) {
+      const int n0 = (ke - kb + 1) >> 1;
+      if (half == 0) ke = kb + n0;
+      else kb += n0;
+    }
+  };
 
   // p = exp2(c * s + (c * b - m_ref)): one FMA per score, c = scale*log2(e),
   // b the block's per-row constant, m_ref the row's reference (log2 units)
@@ -681,8 +699,11 @@ void relattn_fwd_kernel(FwdArgs a) {
   };
   // ALiBi's order needs the exact tile range, so its early copies wait for
   // a per-sequence valid length
+  // (with a key split, a valid length moves the halves' boundary, so the
+  // early copies wait for it too)
   const bool early_copies =
-      KIND == 3 ? a.kv_valid_len == nullptr : (a.n_splits == 1 || a.kv_valid_len == nullptr);
+      (KIND == 3 || KS == 2) ? a.kv_valid_len == nullptr
+                             : (a.n_splits == 1 || a.kv_valid_len == nullptr);
   // Only the first tile goes out here; the others follow the register loads
   // below.  Memory loads retire in order, so a wait for those registers
   // would otherwise also wait for every tile issued before them (with four
@@ -692,12 +713,14 @@ void relattn_fwd_kernel(FwdArgs a) {
     const int n_kt0 = (causal_end + kBK - 1) / kBK;
     const int per0 = (n_kt0 + a.n_splits - 1) / a.n_splits;
     early_beg0 = min(n_kt0, split * per0);
-    early_n0 = min(n_kt0, early_beg0 + per0) - early_beg0;
+    int early_end0 = min(n_kt0, early_beg0 + per0);
+    half_range(early_beg0, early_end0);
+    early_n0 = early_end0 - early_beg0;
     if (early_n0 > 0) {
       Dma dma;
-      dma.init(wave, lane);
-      dma.issue(Kg, Vg, a.Lk, tile_at(0, early_beg0, early_beg0 + early_n0) * kBK, smem,
-                L.tile_bytes, wave, lane);
+      dma.init(wq, lane);
+      dma.issue(Kg, Vg, a.Lk, tile_at(0, early_beg0, early_beg0 + early_n0) * kBK, sbase,
+                L.tile_bytes, wq, lane);
     }
   }
 
@@ -787,8 +810,13 @@ void relattn_fwd_kernel(FwdArgs a) {
   const int kv_end = min(kv_lim, causal_end);
   const int n_kt = kv_end > 0 ? (kv_end + kBK - 1) / kBK : 0;
   const int per_split = (n_kt + a.n_splits - 1) / a.n_splits;
-  const int kt_begin = min(n_kt, split * per_split);
-  const int kt_end = min(n_kt, kt_begin + per_split);
+  int kt_begin = min(n_kt, split * per_split);
+  int kt_end = min(n_kt, kt_begin + per_split);
+  // loop steps of the workgroup (every wave runs them all and meets every
+  // tile barrier; with a key split, half 1 idles after its last tile when it
+  // has one tile fewer than half 0)
+  const int n_steps = KS == 2 ? (kt_end - kt_begin + 1) >> 1 : kt_end - kt_begin;
+  half_range(kt_begin, kt_end);
   const int n_my = kt_end - kt_begin;
 
   // ---- the rest of the early tile copies, once the registers' loads (and
@@ -797,12 +825,12 @@ void relattn_fwd_kernel(FwdArgs a) {
     if (early_copies && early_n0 > 1) {
       wait_vmcnt<0>();
       Dma dma;
-      dma.init(wave, lane);
+      dma.init(wq, lane);
 #pragma unroll
       for (int s = 1; s < AHEAD; ++s)
         if (s < early_n0)
           dma.issue(Kg, Vg, a.Lk, tile_at(s, early_beg0, early_beg0 + early_n0) * kBK,
-                    smem + s * L.stage_bytes, L.tile_bytes, wave, lane);
+                    sbase + s * L.stage_bytes, L.tile_bytes, wq, lane);
     }
   }
 
@@ -918,12 +946,12 @@ void relattn_fwd_kernel(FwdArgs a) {
   // ---- start streaming the first key tiles of a split key range ------------
   if (!early_copies) {
     Dma dma;
-    dma.init(wave, lane);
+    dma.init(wq, lane);
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s)
       if (s < n_my)
-        dma.issue(Kg, Vg, a.Lk, tile_at(s, kt_begin, kt_end) * kBK, smem + s * L.stage_bytes,
-                  L.tile_bytes, wave, lane);
+        dma.issue(Kg, Vg, a.Lk, tile_at(s, kt_begin, kt_end) * kBK, sbase + s * L.stage_bytes,
+                  L.tile_bytes, wq, lane);
   }
 
   // ---- band-row ring (DeBERTa Kr, Transformer-XL E): ring index
@@ -1048,6 +1076,7 @@ void relattn_fwd_kernel(FwdArgs a) {
   // Runs of equal class go through a loop of their own, so the lean loops
   // are not burdened with the registers of the general one.
   auto tile_class = [&](const int r) -> int {
+    if (KS == 2 && r >= n_my) return 3;  // this half has no tile at step r
     const int k0 = tile_at(r, kt_begin, kt_end) * kBK;
     if (!wave_active || (a.causal && k0 > pw_max_real)) return 3;
     bool far_all = true, near_all = true;
@@ -1133,12 +1162,12 @@ void relattn_fwd_kernel(FwdArgs a) {
         if ((r & 1) == 0 && r + 2 < n_my) {
           constexpr bool KEEP = QB == 1 && D <= 64;
           Dma dma;
-          dma.init(wave, KEEP ? lane : opaque_lane());
+          dma.init(wq, KEEP ? lane : opaque_lane());
 #pragma unroll
           for (int t = 2; t < 4; ++t)
             if (r + t < n_my)
               dma.issue(Kg, Vg, a.Lk, tile_at(r + t, kt_begin, kt_end) * kBK,
-                        smem + stage_of(r + t) * L.stage_bytes, L.tile_bytes, wave, lane);
+                        sbase + stage_of(r + t) * L.stage_bytes, L.tile_bytes, wq, lane);
         }
       } else if (r + NS - 1 < n_my) {
         // copy offsets: kept in registers across tiles with one query block
@@ -1147,9 +1176,9 @@ void relattn_fwd_kernel(FwdArgs a) {
         // variant)
         constexpr bool KEEP = QB == 1 && D <= 64 && !(KIND == 2 && NW == 4);
         Dma dma;
-        dma.init(wave, KEEP ? lane : opaque_lane());
+        dma.init(wq, KEEP ? lane : opaque_lane());
         dma.issue(Kg, Vg, a.Lk, tile_at(r + NS - 1, kt_begin, kt_end) * kBK,
-                  smem + stage_of(r + NS - 1) * L.stage_bytes, L.tile_bytes, wave, lane);
+                  sbase + stage_of(r + NS - 1) * L.stage_bytes, L.tile_bytes, wq, lane);
       }
     };
     // a pipelined tile issues them after its first scores, so that its
@@ -1160,7 +1189,7 @@ void relattn_fwd_kernel(FwdArgs a) {
       if (r + 1 < n_my) ring_fill(-64 * (kt + 1), lane);
     }
     if constexpr (CLS == 3) return;
-    const char* ktile = smem + stage_of(r) * L.stage_bytes;
+    const char* ktile = sbase + stage_of(r) * L.stage_bytes;
     const char* vtile = ktile + L.tile_bytes;
 
     // ---- the tile's query blocks (wave-uniform) ----
@@ -1741,7 +1770,7 @@ void relattn_fwd_kernel(FwdArgs a) {
   using C2 = std::integral_constant<int, 2>;
   using C3 = std::integral_constant<int, 3>;
   int r = 0;
-  while (r < n_my) {
+  while (r < n_steps) {
     const int cls = tile_class(r);
     const int ln = opaque_lane();
     if constexpr (QR_NEXT) {
@@ -1752,20 +1781,58 @@ void relattn_fwd_kernel(FwdArgs a) {
       }
     }
     if (cls == 0) {
-      do { run_tile(C0{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 0);
+      do { run_tile(C0{}, r, ln); ++r; } while (r < n_steps && tile_class(r) == 0);
     } else if (cls == 1) {
       if constexpr (KIND == 0) {
-        do { run_tile(C1{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 1);
+        do { run_tile(C1{}, r, ln); ++r; } while (r < n_steps && tile_class(r) == 1);
       }
     } else if (cls == 2) {
-      do { run_tile(C2{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 2);
+      do { run_tile(C2{}, r, ln); ++r; } while (r < n_steps && tile_class(r) == 2);
     } else {
-      do { run_tile(C3{}, r, ln); ++r; } while (r < n_my && tile_class(r) == 3);
+      do { run_tile(C3{}, r, ln); ++r; } while (r < n_steps && tile_class(r) == 3);
     }
   }
 
   // ---- epilogue -------------------------------------------------------------
   wait_vmcnt<0>();  // no tile load may still be writing LDS when the wave ends
+  if constexpr (KS == 2) {
+    // The halves meet: half 1 hands its running state (per lane: the output
+    // registers, the reference, the partial row sum; lane l of wave wq + NWQ
+    // holds the same query row and head dims as lane l of wave wq) to half 0
+    // through the stage memory, which no wave reads any more.  Half 0 moves
+    // both to the larger reference, 2^(m - M) each, and adds them.
+    constexpr int XS = 16 * NDB + 4;  // floats per lane
+    float* xs = reinterpret_cast<float*>(smem) + (size_t)(wq * 64 + lane) * XS;
+    __syncthreads();  // every wave is done with its stages
+    if (half == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(xs + 16 * db + 4 * g) =
+              f32x4{o[0][db][4 * g], o[0][db][4 * g + 1], o[0][db][4 * g + 2], o[0][db][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(xs + 16 * NDB) = f32x4{m_ref[0], l_run[0], 0.f, 0.f};
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const f32x4 ml = *reinterpret_cast<const f32x4*>(xs + 16 * NDB);
+    const float mb = ml[0], lb = ml[1];
+    const float M = fmaxf(m_ref[0], mb);
+    if (M != NEG_INF) {
+      const float wa = m_ref[0] == NEG_INF ? 0.f : fast_exp2(m_ref[0] - M);
+      const float wb = mb == NEG_INF ? 0.f : fast_exp2(mb - M);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(xs + 16 * db + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[0][db][4 * g + e] = wa * o[0][db][4 * g + e] + wb * x[e];
+        }
+      l_run[0] = wa * l_run[0] + wb * lb;
+      m_ref[0] = M;
+    }
+  }
   if (!wave_active) return;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -2005,6 +2072,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int grid, int lds, hipStream_t 
 
 bool fwd_variant_built(int kind, bool bf, int d, Variant v) {
   if (d == 128) return bf && v.qb == 1 && v.nw == 4;
+  if ((kind == 0 || kind == 3) && v.nw == 8) return bf && v.qb == 1;  // key split
   if ((kind == 2 || kind == 4) && bf && d == 64) return v.qb == 1 && (v.nw == 8 || v.nw == 4);
   if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
   return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
@@ -2020,6 +2088,8 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
   RA_CASE(K, false, 32, QBV, NWV)
   RA_DT(0, 1, 4) RA_DT(1, 1, 4) RA_DT(2, 1, 4) RA_DT(3, 1, 4) RA_DT(4, 1, 4)
   RA_CASE(2, true, 64, 1, 8) RA_CASE(4, true, 64, 1, 8)
+  RA_CASE(0, true, 64, 1, 8) RA_CASE(0, true, 32, 1, 8) RA_CASE(3, true, 64, 1, 8)
+  RA_CASE(3, true, 32, 1, 8)
   RA_CASE(0, true, 128, 1, 4) RA_CASE(1, true, 128, 1, 4) RA_CASE(2, true, 128, 1, 4)
   RA_CASE(3, true, 128, 1, 4) RA_CASE(4, true, 128, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
