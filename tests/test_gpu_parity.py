@@ -894,3 +894,44 @@ def test_txl_large_global_biases(dtype, d, sigma):
     got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
     want = run_oracle(wl, inp)
     check_close(got, want, wl.dtype, f"txl biases sigma {sigma}")
+
+
+@pytest.mark.parametrize("sigma", [1.0, 3.0])
+@pytest.mark.parametrize("causal,qb2", [(True, False), (False, False), (True, True)])
+def test_shaw_large_relative_keys(sigma, causal, qb2):
+    # a_K as large as the keys (sigma 1) and three times larger: the kernel
+    # keeps q.a_K[r] - q.a_K[0] per row in LDS, so a large relative-key term
+    # must still meet the bar ([RPE] "Shaw et al.": logit = q.(k + a_K))
+    wl = _small("shaw", "bf16", 64, clip_k=16, causal=causal, Lq=300, Lk=333)
+    if qb2:
+        wl = wl.replace(B=2, H=256, Lq=256, Lk=300)   # two query blocks per wave
+    inp = make_inputs(wl, seed=26)
+    g = torch.Generator("cpu").manual_seed(27)
+    a_k = (torch.randn(inp["table"].shape, generator=g) * sigma).to(wl.torch_dtype)
+    inp = dict(inp, table=a_k)
+    if qb2:
+        heads, rows = [(0, 0), (1, 255), (0, 128)], list(range(0, 256, 7))
+        got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+        want = run_oracle(wl, inp, heads=heads, rows=rows)
+        sel = np.stack([got[b, h][rows] for b, h in heads])
+        check_close(sel, want, wl.dtype, f"shaw a_K sigma {sigma}")
+    else:
+        got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+        check_close(got, run_oracle(wl, inp), wl.dtype, f"shaw a_K sigma {sigma}")
+
+
+@pytest.mark.parametrize("sigma", [5.0, 20.0])
+def test_t5_large_bias_table(sigma):
+    # bias values far above the scaled scores: the kernel folds bias / scale
+    # into its score accumulator ([T5B]: the bias is added to the logit)
+    for wl in (_small("t5", "bf16", 64, valid_len_range=(1, 333)),
+               _small("t5", "fp32", 64, bidirectional=False, causal=True, Lq=200, q_pos_offset=133)):
+        inp = make_inputs(wl, seed=28)
+        g = torch.Generator("cpu").manual_seed(29)
+        inp = dict(inp, table=torch.randn(inp["table"].shape, generator=g) * sigma)
+        got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+        want = run_oracle(wl, inp)
+        tol = STRESS_TOL[wl.dtype]
+        err = np.abs(got - want)
+        assert np.isfinite(got).all()
+        assert err.max() <= tol[0] and err.mean() <= tol[1], (wl.dtype, sigma, err.max(), err.mean())

@@ -163,10 +163,11 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
   P->scale = p->scale > 0.f ? p->scale : dflt;
 
   // Kernel variant: 4 waves.  DeBERTa: 32 rows per wave (its near-block band
-  // tile takes 8.5 KiB of LDS per wave; two workgroups fit a CU).  T5 / Shaw: 64 rows per wave when there
-  // are enough workgroups to fill two per CU (one LDS fragment then feeds two
-  // MFMAs) and the LDS fits two workgroups per CU, else 32 rows per wave.
-  // float32 always uses 32 rows per wave (its fragments are twice as large).
+  // tile takes 8.5 KiB of LDS per wave; two workgroups fit a CU).  T5 /
+  // ALiBi: 64 rows per wave when there are enough workgroups to fill two per
+  // CU (one LDS fragment then feeds two MFMAs) and the LDS fits two
+  // workgroups per CU, else 32 rows per wave.  float32 always uses 32 rows
+  // per wave (its fragments are twice as large).
   const int BH = p->B * p->H;
   auto lds_for = [&](Variant v, int* total, int* lut_n) -> relattn_status {
     *lut_n = 0;
@@ -190,8 +191,10 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
       p->d == 64)
     var = Variant{8, 1};
   int lds_total = 0, lut_n = 0;
-  if ((p->kind == RELATTN_T5 || p->kind == RELATTN_SHAW || p->kind == RELATTN_ALIBI) && P->bf &&
-      p->d <= 64) {
+  // (Shaw keeps one query block per wave: with its per-row float32
+  // relative-key logits, two blocks would leave one workgroup per CU, and one
+  // block per wave measured as fast as two on the causal 4096-token workload)
+  if ((p->kind == RELATTN_T5 || p->kind == RELATTN_ALIBI) && P->bf && p->d <= 64) {
     const int64_t wgs2 = (int64_t)BH * ((p->Lq + 4 * 64 - 1) / (4 * 64));
     int t2 = 0;
     if (wgs2 >= 2 * kNumCU && lds_for(Variant{4, 2}, &t2, &lut_n) == RELATTN_OK &&

@@ -132,8 +132,7 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //   T5      float lut4[4][lut_stride]: four copies of bias[offset]*log2(e),
 //           copy c shifted by c entries, so any 4 consecutive offsets are one
 //           aligned 16-byte read
-//   SHAW    per wave: arel[rows][2k+2] (input dtype: q.a_K[r] - q.a_K[0]);
-//           per wave: float r2k[rows] (the r = 2k entry, unrounded); per
+//   SHAW    per wave: float arel[rows][2k+2] (q.a_K[r] - q.a_K[0]); per
 //           wave: bin rows [rows][bin_slots] (input dtype), one per query
 //           row of the wave; bf16 only: a_V^T [d][bin_slots]; per wave: a_V
 //           rows 0 and 2k [2][d] (input dtype)
@@ -149,7 +148,7 @@ constexpr int kCbandStride = 68;  // 64 band columns, padded: rows stay 16-byte 
 struct LdsLayout {
   int stage_bytes, tile_bytes, rel_off, total;
   int lut_stride;
-  int arel_stride, arel_wave_bytes, r2k_off, wscr_off, wscr_wave_bytes, avt_off, avend_off;
+  int arel_stride, arel_wave_bytes, wscr_off, wscr_wave_bytes, avt_off, avend_off;
   int deb_wave_floats;
   int ring_off;  // DeBERTa / TXL bf16, d = 64, 8 waves: ring of band rows (kRingRows x 128 B)
 };
@@ -182,9 +181,8 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     const int nbin = shaw_bin_slots(clip_k);
     // even stride: a row read at offset (const - row) walks 33 banks per row
     L.arel_stride = 2 * clip_k + 2;
-    L.arel_wave_bytes = (rows * L.arel_stride * esz + 15) / 16 * 16;
-    L.r2k_off = nw * L.arel_wave_bytes;
-    L.wscr_off = L.r2k_off + nw * rows * 4;
+    L.arel_wave_bytes = (rows * L.arel_stride * 4 + 15) / 16 * 16;  // float32
+    L.wscr_off = nw * L.arel_wave_bytes;
     L.wscr_wave_bytes = rows * shaw_bin_stride(clip_k, esz) * esz;
     L.avt_off = L.wscr_off + nw * L.wscr_wave_bytes;
     L.avend_off = L.avt_off + (bf16 ? d * nbin * 2 : 0);

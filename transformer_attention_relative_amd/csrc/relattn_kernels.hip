@@ -838,7 +838,7 @@ void relattn_fwd_kernel(FwdArgs a) {
   float shaw_right[QB];                              // Shaw: q.(a_K[2k] - a_K[0])
   float shaw_base[QB];                               // Shaw: q.a_K[0], left out of every logit
   float crow_lo[QB], crow_hi[QB];                    // DeBERTa: q.Kr[0], q.Kr[2k-1]
-  T* arel = nullptr;     // Shaw: this wave's relative-key logits (input dtype)
+  float* arel = nullptr; // Shaw: this wave's relative-key logits
   T* wbins = nullptr;    // Shaw: this wave's bin rows, [32 * QB][bin slots]
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = shaw_base[qb] = crow_lo[qb] = crow_hi[qb] = 0.f;
@@ -873,8 +873,7 @@ void relattn_fwd_kernel(FwdArgs a) {
     // arel[row][r] = q.a_K[r] - q.a_K[0], r = 0..2k, by MFMA over blocks of
     // 32 table rows; subtracting the r = 0 value is softmax-neutral and
     // makes every key beyond -k contribute exactly zero.
-    arel = reinterpret_cast<T*>(smem + L.rel_off + wave * L.arel_wave_bytes);
-    float* r2k = reinterpret_cast<float*>(smem + L.rel_off + L.r2k_off) + wave * 32 * QB;
+    arel = reinterpret_cast<float*>(smem + L.rel_off + wave * L.arel_wave_bytes);
     wbins = reinterpret_cast<T*>(smem + L.rel_off + L.wscr_off + wave * L.wscr_wave_bytes);
     const int nrow = 2 * ck + 1;
 #pragma unroll
@@ -890,8 +889,7 @@ void relattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = min(rb * 32 + acc_row(i, hh), nrow);
-          arel[(32 * qb + lq) * L.arel_stride + r] = (T)(acc[i] - base0);
-          if (r == 2 * ck) r2k[32 * qb + lq] = acc[i] - base0;  // kept unrounded
+          arel[(32 * qb + lq) * L.arel_stride + r] = acc[i] - base0;
         }
       }
     }
@@ -915,7 +913,7 @@ void relattn_fwd_kernel(FwdArgs a) {
     }
     wave_lds_fence();
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = r2k[32 * qb + lq];
+    for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = arel[(32 * qb + lq) * L.arel_stride + 2 * ck];
     if constexpr (BF) {
       // a_V^T for the in-window bins: avt[d][r'] = a_V[r' + 1][d], r' < 2k - 1
       const int nb = shaw_bin_slots(ck);
@@ -1292,7 +1290,7 @@ void relattn_fwd_kernel(FwdArgs a) {
           }
         } else if constexpr (KIND == 1) {
           if (CLS == 2 && near[qb]) {
-            const T* ar = arel + (32 * qb + lq) * L.arel_stride;
+            const float* ar = arel + (32 * qb + lq) * L.arel_stride;
             const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
             f32x16 init;
 #pragma unroll
@@ -2075,7 +2073,7 @@ bool fwd_variant_built(int kind, bool bf, int d, Variant v) {
   if ((kind == 0 || kind == 3) && v.nw == 8) return bf && v.qb == 1;  // key split
   if ((kind == 2 || kind == 4) && bf && d == 64) return v.qb == 1 && (v.nw == 8 || v.nw == 4);
   if (kind == 2 || kind == 4) return v.qb == 1 && v.nw == 4;  // kinds 0, 1, 3 below
-  return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf));
+  return v.nw == 4 && (v.qb == 1 || (v.qb == 2 && bf && kind != 1));
 }
 
 hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int grid, int lds,
@@ -2093,7 +2091,6 @@ hipError_t launch_fwd(int kind, bool bf, int d, Variant v, const FwdArgs& a, int
   RA_CASE(0, true, 128, 1, 4) RA_CASE(1, true, 128, 1, 4) RA_CASE(2, true, 128, 1, 4)
   RA_CASE(3, true, 128, 1, 4) RA_CASE(4, true, 128, 1, 4)
   RA_CASE(0, true, 64, 2, 4) RA_CASE(0, true, 32, 2, 4)
-  RA_CASE(1, true, 64, 2, 4) RA_CASE(1, true, 32, 2, 4)
   RA_CASE(3, true, 64, 2, 4) RA_CASE(3, true, 32, 2, 4)
 #undef RA_DT
 #undef RA_CASE
