@@ -21,8 +21,8 @@
 //     accumulator directly as the B operand; the V^T A operand comes from the
 //     row-major V tile through ds_read_b64_tr_b16 (LDS transpose read).
 //   * Online softmax in the exp2 domain with scale*log2(e) folded into one
-//     FMA; the running max is only moved (and the output rescaled) when a new
-//     max exceeds it by more than 2^8, which keeps every exponent <= 8.
+//     FMA; a row's reference max is only moved (and the output rescaled) on
+//     an exact path taken by a block whose lane sum of P exceeds 2^20.
 //   * The relative term never exists as an L x L array: per (query block,
 //     key tile) it is a per-row constant folded into the exponent (saturated
 //     T5 buckets, clipped Shaw / DeBERTa offsets) or it is written into the
@@ -36,9 +36,14 @@
 //     multiplied by a_V with one more MFMA; the two clipped bins take the rest
 //     of the row mass at the end ([RPE] Shaw section).
 //   * DeBERTa near blocks compute the content-to-position band (Kr rows x Q)
-//     and the position-to-content band (K x Qr rows) with MFMA and gather
+//     and the position-to-content band (Qr rows x K) with MFMA and gather
 //     them through per-wave LDS; far blocks reduce to a per-row constant plus
 //     a per-key constant ([DRPE]: every offset beyond +-k uses a boundary row).
+//   * Transformer-XL blocks compute q.E over their 63 distances the same way,
+//     with the bias terms u.k_j and v.E[r] added as float32 constants ([RPE]
+//     Transformer-XL section); ALiBi adds slope * distance.
+//   * Decode-like T5 / ALiBi shapes split each workgroup's key range over two
+//     halves of four waves, merged through LDS at the end.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -1387,8 +1392,6 @@ void relattn_fwd_kernel(FwdArgs a) {
             const T* kr = reinterpret_cast<const T*>(a.table);
             const T* qr = reinterpret_cast<const T*>(a.table2);
             const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
-            // the four table fragments of the block's two bands are requested
-            // together, so their L2 latencies overlap instead of adding up
             // Qr rows delta(-(T0 + 32 nb + lane)) (the position-to-content
             // band's A operand); the first half may have been requested by
             // the previous block
