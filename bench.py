@@ -326,12 +326,16 @@ def cpu_baseline(wl: Workload, inp, budget_s: float = 15.0):
 
 # ----------------------------------------------------------------------------
 
+MIN_TIME_MS = 200.0
+
+
 def measure(name: str, steps: int, warmup: int, use_graph: bool, cold: bool = False):
     """Time one workload; returns its record (median of the replays and
     their spread) and its seeded inputs."""
     wl = WORKLOADS[name]
     inp, dev, out, step = _prepare(wl)
-    per_step, wall_ms, graphed = time_steps(step, steps, warmup, use_graph)
+    per_step, wall_ms, graphed = time_steps(step, steps, warmup, use_graph,
+                                            min_total_ms=MIN_TIME_MS)
     flops, nbytes = counted_work(wl, inp["kv_valid_len"])
     ms = float(np.median(per_step))
     tflops = flops / (ms * 1e-3) / 1e12
@@ -384,6 +388,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--min-time-ms", type=float, default=200.0,
+                    help="replay the timed steps until this much GPU time is covered "
+                         "(at least 5 replays; short profiler runs lower it)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other bf16 workloads in the JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -400,6 +407,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    global MIN_TIME_MS
+    MIN_TIME_MS = args.min_time_ms
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(args.steps, 1))
         return
