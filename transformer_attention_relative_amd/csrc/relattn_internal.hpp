@@ -111,9 +111,12 @@ RELATTN_HD constexpr int key_split(int kind, int nw) {
   return ((kind == 0 || kind == 3) && nw == 8) ? 2 : 1;
 }
 
-// Shaw bins strictly inside the clip window (offsets -k+1 .. k-1), padded to
-// whole MFMA contraction chunks.
-RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k - 1) + 15) / 16 * 16; }
+// Shaw bin slots of a query row: slot s holds the probability of the key at
+// offset s - k for the offsets strictly inside the clip window (s = 1 ..
+// 2k-1, the a_V row index); slots 0 and 2k take the keys at offsets <= -k
+// and >= k (overwritten, never read as bins); padded to whole MFMA
+// contraction chunks.
+RELATTN_HD constexpr int shaw_bin_slots(int clip_k) { return ((2 * clip_k + 1) + 15) / 16 * 16; }
 
 // Row stride (elements) of the Shaw bin rows in LDS: the slots plus 16 bytes,
 // an odd multiple of 16 bytes, so that the per-lane bin stores of the 32
@@ -134,7 +137,8 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //           aligned 16-byte read
 //   SHAW    per wave: float arel[rows][2k+2] (q.a_K[r] - q.a_K[0]); per
 //           wave: bin rows [rows][bin_slots] (input dtype), one per query
-//           row of the wave; bf16 only: a_V^T [d][bin_slots]; per wave: a_V
+//           row of the wave; bf16 only: a_V^T [d][bin_slots] (column s =
+//           a_V row s for s = 1 .. 2k-1, zero elsewhere); per wave: a_V
 //           rows 0 and 2k [2][d] (input dtype)
 //   DEBERTA per wave: float band[32][kCbandStride], the content-to-position
 //           band [query][m] and then the position-to-content band [key][n];

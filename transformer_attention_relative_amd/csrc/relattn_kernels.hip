@@ -920,7 +920,7 @@ void relattn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) shaw_right[qb] = arel[(32 * qb + lq) * L.arel_stride + 2 * ck];
     if constexpr (BF) {
-      // a_V^T for the in-window bins: avt[d][r'] = a_V[r' + 1][d], r' < 2k - 1
+      // a_V^T for the in-window bins: avt[d][s] = a_V[s][d], s = 1 .. 2k-1
       const int nb = shaw_bin_slots(ck);
       T* avt = reinterpret_cast<T*>(smem + L.rel_off + L.avt_off);
       const int nch = (2 * ck - 1) * (D / 8);
@@ -930,12 +930,16 @@ void relattn_fwd_kernel(FwdArgs a) {
         if (e < nch) {
           const int r = e / (D / 8), d0 = 8 * (e % (D / 8));
 #pragma unroll
-          for (int q = 0; q < 8; ++q) avt[(d0 + q) * nb + r] = avt_ch[c][q];
+          for (int q = 0; q < 8; ++q) avt[(d0 + q) * nb + r + 1] = avt_ch[c][q];
         }
       }
-      // the padding bins 2k-1 .. nb-1 meet zero rows
-      const int npad = nb - (2 * ck - 1);
-      for (int e = tid; e < D * npad; e += 64 * NW) avt[(e / npad) * nb + 2 * ck - 1 + e % npad] = (T)0.f;
+      // slot 0 and slots 2k .. nb-1 (the out-of-window slots and the padding)
+      // meet zero rows
+      const int npad = nb - 2 * ck;
+      for (int e = tid; e < D * (npad + 1); e += 64 * NW) {
+        const int dd = e / (npad + 1), x = e % (npad + 1);
+        avt[dd * nb + (x == 0 ? 0 : 2 * ck - 1 + x)] = (T)0.f;
+      }
     }
   } else if constexpr (KIND == 2) {
 #pragma unroll
@@ -1039,28 +1043,36 @@ void relattn_fwd_kernel(FwdArgs a) {
       const int nbin = shaw_bin_slots(ck);
       T* wrow = wbins + (32 * qb + lq) * shaw_bin_stride(ck, (int)sizeof(T));
       wave_lds_fence();
+      // the mass inside the window, summed from the bins themselves (the
+      // two out-of-window slots left out)
+      float win = 0.f;
       if constexpr (BF) {
         const bf16* avt = reinterpret_cast<const bf16*>(smem + L.rel_off + L.avt_off);
         for (int cb = 0; cb < nbin / 16; ++cb) {
           const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 16 * cb + 8 * hh);
+          win = sum_bf16x8(wf, win);
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
             const bf16x8 vf = *reinterpret_cast<const bf16x8*>(avt + (32 * db + lq) * nbin + 16 * cb + 8 * hh);
             o[qb][db] = mma_bf16(vf, wf, o[qb][db]);
           }
         }
+        if (hh == 0) win -= (float)wrow[0] + (float)wrow[2 * ck];
       } else {
         const float* av = reinterpret_cast<const float*>(a.table2);
         for (int cb = 0; cb < nbin / 2; ++cb) {
           const int rr = 2 * cb + hh;
+          const bool in_win = rr >= 1 && rr < 2 * ck;
           const float wv = wrow[rr];
+          win += in_win ? wv : 0.f;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const float vv = rr < 2 * ck - 1 ? av[(size_t)(rr + 1) * D + 32 * db + lq] : 0.f;
+            const float vv = in_win ? av[(size_t)rr * D + 32 * db + lq] : 0.f;
             o[qb][db] = mma_f32(vv, wv, o[qb][db]);
           }
         }
       }
+      win_run[qb] += win;
       wave_lds_fence();
       constexpr int EPV = 16 / sizeof(T);
       f32x4* zp = reinterpret_cast<f32x4*>(wrow + hh * (nbin / 2));
@@ -1599,26 +1611,31 @@ void relattn_fwd_kernel(FwdArgs a) {
             // own bin (each offset belongs to exactly one key of a row, so a
             // bin is assigned once); the bins are multiplied by a_V when the
             // row is done or before its running state is rescaled
-            const int nbin = shaw_bin_slots(ck);
+            // Branch-free: the key at offset o stores to slot clamp(o + k,
+            // 0, 2k), so keys outside the window land in the slots 0 and 2k
+            // (never read as bins); the window's mass is summed from the
+            // bins when they are applied
             T* wrow = wbins + (32 * qb + lq) * shaw_bin_stride(ck, (int)sizeof(T));
-            // Branch-free: keys outside the window store to the row's last
-            // slot, a padding slot (2k - 1 < bin slots) that meets a zero
-            // a_V^T row in the bin product.
-            float win = 0.f, lr = 0.f;
             const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int offk = obase + acc_row(i, 0);
-              float pv;
-              if constexpr (BF) pv = (float)pf[qb][i >> 3][i & 7];
-              else pv = s[qb][i];
-              const bool in_win = offk > -ck && offk < ck;
-              wrow[in_win ? offk + ck - 1 : nbin - 1] = (T)pv;
-              win += in_win ? pv : 0.f;
-              lr += offk >= ck ? pv : 0.f;
+              const int slot = min(max(obase + ck + acc_row(i, 0), 0), 2 * ck);
+              if constexpr (BF) wrow[slot] = pf[qb][i >> 3][i & 7];
+              else wrow[slot] = s[qb][i];
             }
-            win_run[qb] += win;
-            lr_run[qb] += lr;
+            // keys at offset >= k (later keys, all hidden under a causal
+            // mask) take bin 2k
+            if (!a.causal) {
+              float lr = 0.f;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                float pv;
+                if constexpr (BF) pv = (float)pf[qb][i >> 3][i & 7];
+                else pv = s[qb][i];
+                lr += obase + acc_row(i, 0) >= ck ? pv : 0.f;
+              }
+              lr_run[qb] += lr;
+            }
             bins_dirty[qb] = true;
           }
         }
