@@ -18,7 +18,8 @@ Readings taken where the pages leave a step open (also listed in the design
 notes of the repository):
   * T5 logits are q.k * scale plus the bias; the bias itself is not scaled.
   * T5 table layout is [num_buckets, H].
-  * Shaw: "scaled as usual" = the whole q.(k + a_K) is multiplied by scale.
+  * Shaw: the page leaves the scaling implicit; the whole q.(k + a_K) is
+    multiplied by scale.
   * DeBERTa: c2p = q_i . Kr[delta(i,j)], p2c = k_j . Qr[delta(j,i)], the sum
     of the three terms times 1/sqrt(3d), d = head dimension.
   * ALiBi ([RPE] "ALiBi and RoPE: the two endpoints": T5 with the table

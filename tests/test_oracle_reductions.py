@@ -286,7 +286,7 @@ def test_vectorised_equals_bruteforce(kind, Lq, Lk, d, q_off, k_off, causal, bid
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_alibi_is_t5_with_a_linear_table(causal):
-    # [RPE] "ALiBi and RoPE": ALiBi is T5 with the table removed, a slope per
+    # [RPE] "ALiBi and RoPE": ALiBi is T5 without a learned table, a slope per
     # head times the distance.  Inside T5's exact range (distance < 8 at
     # bidirectional 32/128, < 16 causal) a T5 table whose exact slots hold
     # slope * distance gives the same logits, so the outputs agree.
