@@ -22,8 +22,8 @@ notes of the repository):
     multiplied by scale.
   * DeBERTa: c2p = q_i . Kr[delta(i,j)], p2c = k_j . Qr[delta(j,i)], the sum
     of the three terms times 1/sqrt(3d), d = head dimension.
-  * ALiBi ([RPE] "ALiBi and RoPE: the two endpoints": T5 with the table
-    removed, a fixed slope per head times the distance): bias = slope[h] *
+  * ALiBi ([RPE] "ALiBi and RoPE: the two endpoints": T5 without a learned
+    table, a fixed slope per head times the distance): bias = slope[h] *
     |key position - query position|, added after scaling like T5's bias;
     the slope carries its sign (negative slopes penalise distance).
   * Transformer-XL ([RPE] "Transformer-XL: four terms and two global
