@@ -6,6 +6,7 @@ accumulation inside the kernels).
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -528,7 +529,9 @@ def _random_case(i):
     return Workload(**kw)
 
 
-RANDOM_CASES = [_random_case(i) for i in range(50)]
+# 300 configurations by default (about 5 s); a longer sweep with
+# RELATTN_RANDOM_CASES=<n>
+RANDOM_CASES = [_random_case(i) for i in range(int(os.environ.get("RELATTN_RANDOM_CASES", "300")))]
 
 
 @pytest.mark.parametrize("wl", RANDOM_CASES, ids=lambda w: _case_id(w) + f"-B{w.B}H{w.H}")
