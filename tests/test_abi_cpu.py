@@ -303,3 +303,43 @@ def test_noalloc_scratch_size_matches_header():
     src = open(HEADER).read()
     m = re.search(r"#define RELATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == ra.binding.NOALLOC_SCRATCH_BYTES
+
+
+def _supported_configs():
+    """Every kind at the extremes of its supported parameters (head widths,
+    dtypes, clip windows, T5 bucket geometry) and of the problem shapes that
+    pick different kernel variants (decode-like, key-split, two query blocks
+    per wave, many heads)."""
+    shapes = [dict(B=1, H=2, Lq=1, Lk=4096, q_pos_offset=4095, causal=True),  # decode: split keys
+              dict(B=4, H=16, Lq=128, Lk=4096, q_pos_offset=3968, causal=True),  # key-split halves
+              dict(B=8, H=16, Lq=2048, Lk=2048),                                 # many workgroups
+              dict(B=1, H=1, Lq=33, Lk=65)]                                      # ragged, tiny
+    widths = [("bf16", 32), ("bf16", 64), ("bf16", 128), ("fp32", 32), ("fp32", 64)]
+    out = []
+    for dtype, d in widths:
+        for shp in shapes:
+            for nb, md, bidir in [(2, 4, False), (32, 128, True), (64, 2048, True), (8, 8, True)]:
+                out.append(dict(kind="t5", dtype=dtype, d=d, table=FAKE, num_buckets=nb,
+                                max_distance=md, bidirectional=bidir and not shp.get("causal"), **shp))
+            for k in (1, 16, 32):
+                out.append(dict(kind="shaw", dtype=dtype, d=d, table=FAKE, table2=FAKE, clip_k=k, **shp))
+            for k in (1, 63, 64, 512, 65536):
+                out.append(dict(kind="deberta", dtype=dtype, d=d, table=FAKE, table2=FAKE, clip_k=k, **shp))
+            out.append(dict(kind="alibi", dtype=dtype, d=d, table=FAKE, **shp))
+            if shp.get("causal"):
+                far = shp.get("q_pos_offset", 0) + shp["Lq"]
+                out.append(dict(kind="txl", dtype=dtype, d=d, table=FAKE, table2=FAKE,
+                                clip_k=far, **shp))
+    return out
+
+
+def test_every_supported_configuration_plans():
+    # the host plan picks a built kernel variant whose LDS fits a CU (160 KiB)
+    # for every kind at the extremes of its parameters; a layout change that
+    # overflows LDS or a variant missing from the launch table shows up here
+    # as RELATTN_ERR_UNSUPPORTED
+    for kw in _supported_configs():
+        try:
+            ra.relattn_workspace_bytes(_params(**kw))
+        except Exception as e:  # noqa: BLE001 - report the failing configuration
+            raise AssertionError(f"{kw}: {e}") from e
