@@ -519,11 +519,11 @@ def _random_case(i):
         kw["valid_len_range"] = (0, Lk)
     if kind == "t5":
         kw.update(num_buckets=int(rng.choice([8, 16, 32, 64])), bidirectional=not causal)
-        kw["max_distance"] = int(rng.choice([kw["num_buckets"], 128, 1000]))
+        kw["max_distance"] = int(rng.choice([kw["num_buckets"], 128, 1000, 2048]))
     elif kind == "shaw":
         kw["clip_k"] = int(rng.choice([1, 4, 16, 32]))
     elif kind == "deberta":
-        kw["clip_k"] = int(rng.choice([1, 8, 64, 512]))
+        kw["clip_k"] = int(rng.choice([1, 8, 64, 512, 65536]))
     elif kind == "txl":
         kw["clip_k"] = max(1, qpo + Lq - kpo) + int(rng.integers(0, 50))
     return Workload(**kw)
