@@ -123,8 +123,13 @@ def test_fwd_workspace_too_small(lib):
 def test_workspace_sizes():
     p = _params(kind="t5", table=FAKE, B=8, H=12, Lq=512, Lk=512)
     assert ra.relattn_workspace_bytes(p) == 0          # enough workgroups, no split
+    # DeBERTa in bfloat16 forms its per-key constants inside the forward
+    # kernel; in float32 they come from the pre-pass, 8 bytes per (head, key)
     p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=512, B=8, H=12,
                 Lq=2048, Lk=2048)
+    assert ra.relattn_workspace_bytes(p) == 0
+    p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=512, B=8, H=12,
+                Lq=2048, Lk=2048, dtype="fp32")
     assert ra.relattn_workspace_bytes(p) == 96 * 2048 * 8   # per-key constants, no split
     # decode-like shape: few query tiles over a long key range -> split-KV partials
     p = _params(kind="t5", table=FAKE, B=4, H=16, Lq=128, Lk=4096, q_pos_offset=3968,
@@ -157,7 +162,7 @@ def test_workspace_sizes():
     assert ra.relattn_workspace_bytes(p) == 0
     p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=64, d=128, B=4, H=16, Lq=2048,
                 Lk=2048)
-    assert ra.relattn_workspace_bytes(p) == 64 * 2048 * 8
+    assert ra.relattn_workspace_bytes(p) == 0
 
 
 def test_rel_index_validation(lib):
@@ -284,10 +289,11 @@ def test_binding_rel_index_checks():
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch(lib):
-    # DeBERTa's per-key constants of 64 x 16 heads x 4096 keys take 32 MiB,
-    # twice the fixed scratch: refused before any HIP call, with the reason
+    # float32 DeBERTa's per-key constants of 64 x 16 heads x 4096 keys take
+    # 32 MiB, twice the fixed scratch: refused before any HIP call, with the
+    # reason
     p = _params(kind="deberta", table=FAKE, table2=FAKE, clip_k=512, B=64, H=16, Lq=4096,
-                Lk=4096)
+                Lk=4096, dtype="fp32")
     need = ra.relattn_workspace_bytes(p)
     assert need > ra.binding.NOALLOC_SCRATCH_BYTES
     st = lib.relattn_fwd_noalloc(ctypes.byref(p), 0x10000, 0x10000, 0x10000, 0x10000, None)

@@ -14,14 +14,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 # every kind of scratch use: split-KV partials (KV-cache step, one-token
-# decode), per-key constants (DeBERTa), per-key and per-distance constants
-# (Transformer-XL)
+# decode), per-key constants (DeBERTa in float32; in bfloat16 the kernel forms
+# them itself), per-key and per-distance constants (Transformer-XL)
 PAIRS = [
     (WORKLOADS["t5_decoder_kvcache"],
      WORKLOADS["t5_decoder_kvcache"].replace(B=1, H=3, Lk=2000, q_pos_offset=1872)),
     (WORKLOADS["t5_decode_evicted"], WORKLOADS["t5_decode_evicted"].replace(B=2, H=3, Lk=1500)),
-    (WORKLOADS["deberta_k512"].replace(B=4),
-     WORKLOADS["deberta_k512"].replace(B=1, H=2, Lq=700, Lk=900)),
+    (WORKLOADS["deberta_k512"].replace(B=2, dtype="fp32"),
+     WORKLOADS["deberta_k512"].replace(B=1, H=2, Lq=700, Lk=900, dtype="fp32")),
     (WORKLOADS["txl_memory"],
      WORKLOADS["txl_memory"].replace(B=1, H=2, Lq=300, Lk=800, q_pos_offset=500, clip_k=800)),
 ]

@@ -104,6 +104,7 @@ relattn_status t5_plan(int num_buckets, int max_distance, int bidirectional, int
 
 struct Plan {
   bool bf;
+  bool colc;  // the row-constant pre-pass runs before the forward kernel
   float scale;
   Variant var;
   int n_qtiles, n_splits, grid, lds, cu_slots;
@@ -260,9 +261,13 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     P->cu_slots = std::max(1, std::min(by_regs, by_lds));
   }
 
-  // the row-constant pre-pass runs one lane per 16-byte chunk of every
-  // (head, key) row and every (head, encoding row)
-  if ((p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) &&
+  // the row-constant pre-pass (Transformer-XL; DeBERTa in float32: bfloat16
+  // DeBERTa forms its per-key constants with MFMA inside the forward kernel)
+  // runs one lane per 16-byte chunk of every (head, key) row and every
+  // (head, encoding row)
+  const bool colc = p->kind == RELATTN_TXL || (p->kind == RELATTN_DEBERTA && !P->bf);
+  P->colc = colc;
+  if (colc &&
       ((int64_t)BH * p->Lk + (p->kind == RELATTN_TXL ? (int64_t)p->H * p->clip_k : 0)) *
               (p->d * (P->bf ? 2 : 4) / 16) >= ((int64_t)1 << 31))
     return fail(RELATTN_ERR_UNSUPPORTED, "B*H*Lk too large for the row-constant pass");
@@ -274,7 +279,7 @@ relattn_status plan_problem(const relattn_params* p, Plan* P) {
     P->off_part_ml = off;
     off = align256(off + (size_t)splits * BH * p->Lq * 2 * sizeof(float));
   }
-  if (p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) {
+  if (colc) {
     // per-key constants, 8 bytes per (head, key)
     P->off_colc = off;
     off = align256(off + (size_t)BH * p->Lk * 8);
@@ -375,7 +380,7 @@ relattn_status enqueue(const relattn_params* p, const Plan& P, const void* q, co
     for (int m = 0; m < kT5MaxThr; ++m) a.t5_thr[m] = m < P.t5.nthr ? P.t5.thr[m] : INT32_MAX;
   }
   hipError_t e = hipSuccess;
-  if (p->kind == RELATTN_DEBERTA || p->kind == RELATTN_TXL) {
+  if (P.colc) {
     const size_t esz = P.bf ? 2 : 4;
     const char* t2 = reinterpret_cast<const char*>(p->table2);
     ColcArgs ca;

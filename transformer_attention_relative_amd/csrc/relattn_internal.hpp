@@ -143,7 +143,8 @@ RELATTN_HD constexpr int shaw_bin_stride(int clip_k, int esz) {
 //   DEBERTA per wave: float band[32][kCbandStride], the content-to-position
 //           band [query][m] and then the position-to-content band [key][n];
 //           bf16, d = 64, 8 waves: the Kr ring [kRingRows][d] (rows
-//           XOR-swizzled like the K tiles)
+//           XOR-swizzled like the K tiles); bf16: the head's clipped Qr rows
+//           Qr[0] and Qr[2k-1] [2][d]
 //   TXL     per wave: float band[32][kCbandStride], the position band
 //           [query][m]; bf16, d = 64, 8 waves: the E ring, as DeBERTa's
 constexpr int kCbandStride = 68;  // 64 band columns, padded: rows stay 16-byte aligned and
@@ -155,6 +156,7 @@ struct LdsLayout {
   int arel_stride, arel_wave_bytes, wscr_off, wscr_wave_bytes, avt_off, avend_off;
   int deb_wave_floats;
   int ring_off;  // DeBERTa / TXL bf16, d = 64, 8 waves: ring of band rows (kRingRows x 128 B)
+  int qr_off;    // DeBERTa bf16: the clipped Qr rows [2][d]
 };
 
 // The band rows of a workgroup of 8 waves x 32 query rows (DeBERTa's Kr
@@ -197,6 +199,10 @@ RELATTN_HD inline LdsLayout lds_layout(int kind, bool bf16, int d, int qb, int n
     if (band_ring(kind, bf16, d, nw)) {
       L.ring_off = rel_bytes;
       rel_bytes += kRingRows * d * 2;
+    }
+    if (kind == 2 && bf16) {
+      L.qr_off = rel_bytes;
+      rel_bytes += 2 * d * 2;
     }
   }  // ALIBI: nothing beyond the stages
   L.total = L.rel_off + ((rel_bytes + 15) & ~15);

@@ -486,10 +486,14 @@ __device__ __forceinline__ float ref_offset(float cb, float m_ref) {
 }
 
 // DeBERTa blocks whose offsets are all clipped use one Qr row for every pair,
-// so their position-to-content term k_j.Qr[d] is a per-key constant.  The
-// constants come from relattn_colc_kernel (float32 dot products) and enter
-// the score accumulator through one MFMA: A holds the key's constants (as
-// bfloat16 hi + lo pairs, or float32), B selects the side for every query.
+// so their position-to-content term k_j.Qr[d] is a per-key constant.  In
+// bfloat16 the kernel forms it itself: K times a B operand whose every
+// column is that Qr row, four more MFMAs on the block's K fragment (exact
+// products, float32 sums).  In float32 the constants come from
+// relattn_colc_kernel (float32 dot products) and enter the score accumulator
+// through one MFMA: A holds the key's constants, B selects the side for
+// every query.  Transformer-XL's u.k_j takes the same key-constant MFMA with
+// bfloat16 hi + lo pairs.
 template <bool BF>
 struct KeyConst;
 template <>
@@ -948,6 +952,17 @@ void relattn_fwd_kernel(FwdArgs a) {
       crow_lo[qb] = __shfl(acc[0], lq);
       crow_hi[qb] = __shfl(acc[1], lq);
     }
+    if constexpr (BF) {
+      // the head's clipped Qr rows Qr[0] and Qr[2k-1], one 16-byte chunk per
+      // thread (read after the first tile's barrier)
+      constexpr int NCH = D / 8;
+      if (tid < 2 * NCH) {
+        const int row = tid < NCH ? 0 : 2 * ck - 1, c8 = tid % NCH;
+        const T* src = reinterpret_cast<const T*>(a.table2) + ((size_t)row * a.H + h) * D + 8 * c8;
+        *reinterpret_cast<f32x4*>(smem + L.rel_off + L.qr_off + (tid / NCH) * D * 2 + 16 * c8) =
+            *reinterpret_cast<const f32x4*>(src);
+      }
+    }
   }
 
   // ---- start streaming the first key tiles of a split key range ------------
@@ -1152,9 +1167,18 @@ void relattn_fwd_kernel(FwdArgs a) {
     //   of one query block reads the distance rows T0 + 32 tb + m, T0 = T0t -
     //   32 kb (tb = 0, 1; m = lane), so entry t = 1 - kb + tb holds rows T0t +
     //   32 (t - 1) + m (hidden negative distances read row 0)
-    KeyConst<BF> kc[(KIND == 2 || KIND == 4) ? NKB : 1];
+    constexpr bool KEYC = KIND == 4 || (KIND == 2 && !BF);  // per-key constants from the pre-pass
+    KeyConst<BF> kc[KEYC ? NKB : 1];
+    // DeBERTa bfloat16: q.k_j + k_j.Qr[side row] for a block whose offsets
+    // are all clipped to one side: K (A) times Q^T (B) on top of K times the
+    // side's Qr row in every column (B, read from LDS)
+    auto clipped_scores = [&](const TableFrag<BF, D>& kf, const int qb, const int side) -> f32x16 {
+      TableFrag<BF, D> rf;
+      rf.load(reinterpret_cast<const T*>(smem + L.rel_off + L.qr_off) + side * D, hh);
+      return mma_frag<BF, D>(kf, qf[qb], mma_frag0<BF, D>(kf, rf));
+    };
     KeyConst<BF> venc[KIND == 4 ? NKB + 1 : 1];
-    if constexpr ((KIND == 2 || KIND == 4) && CLS != 3) {
+    if constexpr (KEYC && CLS != 3) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kc[kb].load(a.colc, (size_t)bh * a.Lk, min(k0 + 32 * kb + lq, a.Lk - 1), hh);
     }
@@ -1172,7 +1196,7 @@ void relattn_fwd_kernel(FwdArgs a) {
     // the first use of the constants would count only its loads and so also
     // wait for those copies (measured on Transformer-XL with memory: 303 ->
     // 296 us)
-    if constexpr ((KIND == 2 || KIND == 4) && CLS != 3) wait_vmcnt<0>();
+    if constexpr (KEYC && CLS != 3) wait_vmcnt<0>();
     // Lean tiles in bfloat16 run as a software pipeline (below); T5 with two
     // query blocks per wave or 128-wide heads keeps the step loop (the
     // pipeline's extra live registers spill there)
@@ -1414,8 +1438,12 @@ void relattn_fwd_kernel(FwdArgs a) {
           const int side = CLS == 0 ? deb_side[qb] : deb_block_side(qb);
           if (side >= 0) {
             // k_j.Qr[0] (side 0) or k_j.Qr[2k-1] (side 1) for every query
-            s = mma_keyconst<BF>(kc[kb], side, hh);
-            s = mma_frag<BF, D>(kf, qf[qb], s);
+            if constexpr (BF) {
+              s = clipped_scores(kf, qb, side);
+            } else {
+              s = mma_keyconst<BF>(kc[kb], side, hh);
+              s = mma_frag<BF, D>(kf, qf[qb], s);
+            }
           } else {
             // one 32 x kCbandStride float tile per wave, used first for the
             // content-to-position band, then for the position-to-content band
@@ -1692,7 +1720,7 @@ void relattn_fwd_kernel(FwdArgs a) {
             return mma_frag0<BF, D>(kf, qf[qb]);
           }
         } else if constexpr (KIND == 2) {
-          return mma_frag<BF, D>(kf, qf[qb], mma_keyconst<BF>(kc[kb], deb_side[qb], hh));
+          return clipped_scores(kf, qb, deb_side[qb]);
         } else if constexpr (KIND == 3) {
           return mma_frag<BF, D>(kf, qf[qb], mma_keyconst<BF>(alibi_kc, deb_side[qb], hh));
         } else {
