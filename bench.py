@@ -4,8 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one call of the fused forward (every kernel of the path: the
-row-constant pre-pass of DeBERTa and Transformer-XL, the fused attention
-kernel, the split-KV merge) over one batch of seeded synthetic inputs already
+row-constant pre-pass of Transformer-XL, the fused attention kernel, the
+split-KV merge) over one batch of seeded synthetic inputs already
 resident in HBM.  Every figure is the median over timed replays of a HIP
 graph of exactly `--steps` steps (at least 5 replays and 200 ms), with the
 fastest and slowest replay beside it.  Prints one JSON line: the headline is

@@ -183,10 +183,11 @@ relattn_status relattn_fwd_noalloc(const relattn_params *p, const void *q, const
                                    const void *v, void *out, void *stream);
 
 /* Bytes of device workspace relattn_fwd needs for this problem: the split-KV
- * partial results of decode-like shapes; for DEBERTA the per-key
+ * partial results of decode-like shapes; for DEBERTA in FP32 the per-key
  * position-to-content constants of clipped blocks (8 bytes per key and
- * head); for TXL the per-key constants u.k_j (8 bytes per key and head) and
- * the per-distance constants v.E[r] (8 bytes per encoding row and head). */
+ * head; in BF16 the kernel forms them itself); for TXL the per-distance
+ * constants v.E[r] (8 bytes per encoding row and head) and, in FP32, the
+ * per-key constants u.k_j (8 bytes per key and head). */
 relattn_status relattn_workspace_bytes(const relattn_params *p, size_t *bytes);
 
 /*
