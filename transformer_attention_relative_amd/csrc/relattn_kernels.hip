@@ -1033,6 +1033,14 @@ void relattn_fwd_kernel(FwdArgs a) {
   constexpr bool QR_NEXT = KIND == 2 && KR_RING;
   TableFrag<BF, D> qr_next;
   int qr_t0 = -(1 << 30);
+  // ... and this block's first half, the next block's second half (the
+  // next block's T0 is this one's minus 32), tagged with that T0.  Every
+  // near block after the first thus reads one new half from memory, early.
+  // The eight-wave kernel then holds 21 registers in scratch (reloaded in
+  // the band path); measured on DeBERTa k=512 it still runs 1.5% faster
+  // than reading the second half at the block's start.
+  TableFrag<BF, D> qr_carry;
+  int qr_ct0 = -(1 << 30);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -1284,12 +1292,6 @@ void relattn_fwd_kernel(FwdArgs a) {
     // bit mask QM: scores, softmax, P V.  A K fragment and a V fragment read
     // from LDS feed every query block of the step.  Class 2 runs one query
     // block per step so that fewer values are live.
-    // DeBERTa's eight-wave kernel: key block 1 of a tile needs the Qr rows
-    // of distances T0 + 32 .. T0 + 63 of its own T0, which are key block
-    // 0's first half; block 0 leaves them here (they live within the tile
-    // only)
-    TableFrag<BF, D> qr_carry;
-    bool qr_carried = false;
     auto step = [&](auto qm_tag, const int kb) {
       constexpr int QM = decltype(qm_tag)::value;
       const int j0 = k0 + 32 * kb;
@@ -1463,7 +1465,7 @@ void relattn_fwd_kernel(FwdArgs a) {
             TableFrag<BF, D> bfr[2];
             if (QR_NEXT && qr_t0 == T0) bfr[0] = qr_next;
             else bfr[0].load(qr + ((size_t)deberta_delta_dev(-(T0 + lq), ck) * a.H + h) * D, hh);
-            if (QR_NEXT && kb == 1 && qr_carried) bfr[1] = qr_carry;
+            if (QR_NEXT && qr_ct0 == T0) bfr[1] = qr_carry;
             else bfr[1].load(qr + ((size_t)deberta_delta_dev(-(T0 + 32 + lq), ck) * a.H + h) * D, hh);
             // content-to-position: rows Kr[delta(T0 + m)], columns = queries,
             // stored [query][m]
@@ -1516,10 +1518,8 @@ void relattn_fwd_kernel(FwdArgs a) {
               // the next key block's first half: distances T0 - 32 + lane
               qr_next.load(qr + ((size_t)deberta_delta_dev(-(T0 - 32 + lq), ck) * a.H + h) * D, hh);
               qr_t0 = T0 - 32;
-              if (kb == 0) {
-                qr_carry = bfr[0];
-                qr_carried = true;
-              }
+              qr_carry = bfr[0];
+              qr_ct0 = T0 - 32;
             }
             wave_lds_fence();
             // key j0 + jl of query row lq sits at n = lq - jl + 31
@@ -1893,6 +1893,8 @@ void relattn_fwd_kernel(FwdArgs a) {
         // no near block follows within this run: drop the requested Qr rows
         qr_t0 = -(1 << 30);
         qr_next.zero();
+        qr_ct0 = -(1 << 30);
+        qr_carry.zero();
       }
     }
     if (cls == 0) {
