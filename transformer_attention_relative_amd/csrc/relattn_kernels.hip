@@ -1207,8 +1207,13 @@ void relattn_fwd_kernel(FwdArgs a) {
     if constexpr (KEYC && CLS != 3) wait_vmcnt<0>();
     // Lean tiles in bfloat16 run as a software pipeline (below); T5 with two
     // query blocks per wave or 128-wide heads keeps the step loop (the
-    // pipeline's extra live registers spill there)
-    constexpr bool PIPE = CLS != 2 && CLS != 3 && BF && KIND != 4 && !(KIND == 0 && (QB == 2 || D > 64));
+    // pipeline's extra live registers spill there).  Shaw's tiles with
+    // blocks inside the clip window run in the pipeline too (64-wide heads):
+    // their blocks take the relative-key logits as the accumulator's
+    // initial value, the masks, and the bins after the softmax
+    constexpr bool SHAW_NEAR_PIPE = KIND == 1 && CLS == 2 && BF && QB == 1 && D <= 64;
+    constexpr bool PIPE = (CLS != 2 || SHAW_NEAR_PIPE) && CLS != 3 && BF && KIND != 4 &&
+                          !(KIND == 0 && (QB == 2 || D > 64));
     // copies of the tile NS - 1 ahead into the stage of tile r - 1 (free:
     // every wave has passed the barrier above)
     auto issue_next = [&]() {
@@ -1730,6 +1735,30 @@ void relattn_fwd_kernel(FwdArgs a) {
           } else {
             return mma_frag0<BF, D>(kf, qf[qb]);
           }
+        } else if constexpr (KIND == 1 && CLS == 2) {
+          const int j0 = k0 + 32 * kb;
+          f32x16 x;
+          if (near[qb]) {
+            const float* ar = arel + (32 * qb + lq) * L.arel_stride;
+            const int obase = j0 + 4 * hh - pos[qb];  // offset of register 0's key
+            f32x16 init;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) init[i] = (float)ar[shaw_row_dev(obase + acc_row(i, 0), ck)];
+            x = mma_frag<BF, D>(kf, qf[qb], init);
+          } else {
+            x = mma_frag0<BF, D>(kf, qf[qb]);
+          }
+          // hidden keys -inf (blocks that touch the causal diagonal or the
+          // end of the valid keys)
+          const int pq_min = pw_min + 32 * qb;
+          if ((a.causal && j0 + 31 > pq_min) || (j0 + 32 > kv_lim)) {
+            const int last = a.causal ? min(kv_lim - 1, pos[qb]) : kv_lim - 1;
+            const int lim = last - j0 - 4 * hh;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (acc_row(i, 0) > lim) x[i] = NEG_INF;
+          }
+          return x;
         } else if constexpr (KIND == 2) {
           return clipped_scores(kf, qb, deb_side[qb]);
         } else if constexpr (KIND == 3) {
@@ -1859,6 +1888,29 @@ void relattn_fwd_kernel(FwdArgs a) {
         l_run[qb] += ls;
         if constexpr (KIND == 1) {
           if (far_right[qb]) lr_run[qb] += ls;
+        }
+        if constexpr (KIND == 1 && CLS == 2) {
+          if (near[qb]) {
+            // keys inside the window: their probability to the row's own bin
+            // (slot clamp(offset + k, 0, 2k): keys outside the window land
+            // in the unread slots 0 and 2k); keys at offset >= k, only
+            // without a causal mask, to bin 2k
+            T* wrow = wbins + (32 * qb + lq) * shaw_bin_stride(ck, (int)sizeof(T));
+            const int obase = k0 + 32 * kb + 4 * hh - pos[qb];  // offset of register 0's key
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int slot = min(max(obase + ck + acc_row(i, 0), 0), 2 * ck);
+              wrow[slot] = pb[g & 1][i >> 3][i & 7];
+            }
+            if (!a.causal) {
+              float lr = 0.f;
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                lr += obase + acc_row(i, 0) >= ck ? (float)pb[g & 1][i >> 3][i & 7] : 0.f;
+              lr_run[qb] += lr;
+            }
+            bins_dirty[qb] = true;
+          }
         }
       }
       if constexpr (QB == 1 && !KPRE) load_v(NKB - 1);
