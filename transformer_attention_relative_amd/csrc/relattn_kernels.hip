@@ -1028,17 +1028,18 @@ void relattn_fwd_kernel(FwdArgs a) {
   int txl_t0 = -(1 << 30);  // no block yet
   // DeBERTa (same kernel): the first half of the Qr rows of the wave's next
   // key block (distances T0 - 32 ..), requested right after this block's
-  // band products, so its latency hides behind this block's softmax and
+  // band gathers, so its latency hides behind this block's softmax and
   // P V; tagged with the block's T0
   constexpr bool QR_NEXT = KIND == 2 && KR_RING;
   TableFrag<BF, D> qr_next;
   int qr_t0 = -(1 << 30);
   // ... and this block's first half, the next block's second half (the
   // next block's T0 is this one's minus 32), tagged with that T0.  Every
-  // near block after the first thus reads one new half from memory, early.
-  // The eight-wave kernel then holds 21 registers in scratch (reloaded in
-  // the band path); measured on DeBERTa k=512 it still runs 1.5% faster
-  // than reading the second half at the block's start.
+  // near block after the first thus reads one new half from memory, early
+  // (requested once the block's band gathers are done, which leaves the
+  // eight-wave kernel 7 registers in scratch instead of 21 at the same
+  // speed); measured on DeBERTa k=512 it runs 1.5% faster than reading the
+  // second half at the block's start.
   TableFrag<BF, D> qr_carry;
   int qr_ct0 = -(1 << 30);
 #pragma unroll
@@ -1520,9 +1521,6 @@ void relattn_fwd_kernel(FwdArgs a) {
               }
             }
             if constexpr (QR_NEXT) {
-              // the next key block's first half: distances T0 - 32 + lane
-              qr_next.load(qr + ((size_t)deberta_delta_dev(-(T0 - 32 + lq), ck) * a.H + h) * D, hh);
-              qr_t0 = T0 - 32;
               qr_carry = bfr[0];
               qr_ct0 = T0 - 32;
             }
@@ -1535,6 +1533,11 @@ void relattn_fwd_kernel(FwdArgs a) {
               for (int i = 0; i < 16; ++i) init[i] = cg[i] + prow[acc_row(i, hh) * (kCbandStride - 1)];
             }
             wave_lds_fence();  // the next block overwrites the tile
+            if constexpr (QR_NEXT) {
+              // the next key block's first half: distances T0 - 32 + lane
+              qr_next.load(qr + ((size_t)deberta_delta_dev(-(T0 - 32 + lq), ck) * a.H + h) * D, hh);
+              qr_t0 = T0 - 32;
+            }
             s = mma_frag<BF, D>(kf, qf[qb], init);
           }
         }
