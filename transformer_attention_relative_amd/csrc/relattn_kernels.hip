@@ -38,7 +38,9 @@
 //   * DeBERTa near blocks compute the content-to-position band (Kr rows x Q)
 //     and the position-to-content band (Qr rows x K) with MFMA and gather
 //     them through per-wave LDS; far blocks reduce to a per-row constant plus
-//     a per-key constant ([DRPE]: every offset beyond +-k uses a boundary row).
+//     a per-key constant ([DRPE]: every offset beyond +-k uses a boundary
+//     row), the latter formed in bfloat16 as K times the boundary Qr row by
+//     MFMA.
 //   * Transformer-XL blocks compute q.E over their 63 distances the same way,
 //     with the bias terms u.k_j and v.E[r] added as float32 constants ([RPE]
 //     Transformer-XL section); ALiBi adds slope * distance.
@@ -1029,7 +1031,7 @@ void relattn_fwd_kernel(FwdArgs a) {
   // DeBERTa (same kernel): the first half of the Qr rows of the wave's next
   // key block (distances T0 - 32 ..), requested right after this block's
   // band gathers, so its latency hides behind this block's softmax and
-  // P V; tagged with the block's T0
+  // P V; tagged with the T0 of the block it serves
   constexpr bool QR_NEXT = KIND == 2 && KR_RING;
   TableFrag<BF, D> qr_next;
   int qr_t0 = -(1 << 30);
