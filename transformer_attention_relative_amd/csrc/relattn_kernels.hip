@@ -2143,59 +2143,69 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(CombineArgs a) {
 // is CPR 16-byte chunks; CPR consecutive lanes take one row (lane c its chunk
 // c), so a wave reads 64 / CPR whole rows, one contiguous run per load when
 // the rows are adjacent, and the partial dot products meet by lane exchanges.
-// The entries of job 0 come first, then those of job 1.
+// Grid: x = blocks of kColcPasses * 256 / CPR rows of one group (each lane
+// group takes kColcPasses rows, requested together), y = groups (strided
+// when there are more groups than the grid's y extent), z = job; no lane
+// divides.  A job without a second vector multiplies by zeros.
+constexpr int kColcPasses = 4;  // Transformer-XL with memory: 293.7 -> 288.5 us with the 3-D grid
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void relattn_colc_kernel(ColcArgs a) {
   using T = typename std::conditional<BF, bf16, float>::type;
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / EPV;         // chunks per row (4 .. 16)
   static_assert(CPR >= 2 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "chunks per row");
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int c = (int)(t % CPR);
-  int64_t idx = t / CPR;               // entry (row) of this group of lanes
-  const int64_t n0 = (int64_t)a.job[0].G * a.job[0].R;
-  const int64_t n1 = a.njobs > 1 ? (int64_t)a.job[1].G * a.job[1].R : 0;
-  // every lane of a row group stays for the exchanges; a group past the last
-  // entry computes nothing and stores nothing
-  const bool live = idx < n0 + n1;
-  int jb = 0;
-  if (idx >= n0) {
-    idx -= n0;
-    jb = 1;
-  }
-  float s0 = 0.f, s1 = 0.f;
-  const ColcJob& j = a.job[jb];
-  if (live) {
-    const int g = (int)(idx / j.R), r = (int)(idx - (int64_t)g * j.R);
+  constexpr int RPB = 256 / CPR;       // rows per workgroup and pass
+  constexpr int NP = kColcPasses;      // passes: rows r, r + RPB, ... of one lane group
+  const ColcJob& j = a.job[blockIdx.z];
+  const int c = threadIdx.x % CPR;
+  const int r0 = blockIdx.x * RPB * NP + threadIdx.x / CPR;  // first row within the group
+  for (int g = blockIdx.y; g < j.G; g += gridDim.y) {  // wave-uniform
     const int h = g % j.H;
-    const T* x = reinterpret_cast<const T*>(j.x) + ((int64_t)g * j.x_sg + (int64_t)r * j.x_sr) * D + c * EPV;
-    const f32x4 kx = *reinterpret_cast<const f32x4*>(x);
     const f32x4 ax = *reinterpret_cast<const f32x4*>(reinterpret_cast<const T*>(j.a0) + (size_t)h * D + c * EPV);
-    const T* ke = reinterpret_cast<const T*>(&kx);
-    const T* ae = reinterpret_cast<const T*>(&ax);
+    f32x4 bx = {};
+    if (j.a1) bx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const T*>(j.a1) + (size_t)h * D + c * EPV);
+    // the pass rows' chunks are requested together; a row past the last
+    // computes nothing and stores nothing, but its lanes stay for the
+    // exchanges
+    f32x4 kx[NP];
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) s0 = fmaf((float)ke[e], (float)ae[e], s0);
-    if (j.a1) {
-      const f32x4 bx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const T*>(j.a1) + (size_t)h * D + c * EPV);
-      const T* be = reinterpret_cast<const T*>(&bx);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) s1 = fmaf((float)ke[e], (float)be[e], s1);
+    for (int p = 0; p < NP; ++p) {
+      const int r = r0 + p * RPB;
+      kx[p] = {};
+      if (r < j.R)
+        kx[p] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const T*>(j.x) +
+                                                ((int64_t)g * j.x_sg + (int64_t)r * j.x_sr) * D + c * EPV);
     }
-  }
-  // sum over the CPR lanes of the row (a fixed order, so the result does not
-  // depend on the launch)
 #pragma unroll
-  for (int m = 1; m < CPR; m <<= 1) {
-    s0 += __shfl_xor(s0, m);
-    s1 += __shfl_xor(s1, m);
-  }
-  if (!live || c != 0) return;
-  if constexpr (BF) {
-    const bf16 h0 = (bf16)s0, h1 = (bf16)s1;
-    const bf16x4 y = {h0, (bf16)(s0 - (float)h0), h1, (bf16)(s1 - (float)h1)};
-    reinterpret_cast<bf16x4*>(j.out)[idx] = y;
-  } else {
-    reinterpret_cast<f32x2*>(j.out)[idx] = f32x2{s0, s1};
+    for (int p = 0; p < NP; ++p) {
+      const int r = r0 + p * RPB;
+      const T* ke = reinterpret_cast<const T*>(&kx[p]);
+      const T* ae = reinterpret_cast<const T*>(&ax);
+      const T* be = reinterpret_cast<const T*>(&bx);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        s0 = fmaf((float)ke[e], (float)ae[e], s0);
+        s1 = fmaf((float)ke[e], (float)be[e], s1);
+      }
+      // sum over the CPR lanes of the row (a fixed order, so the result
+      // does not depend on the launch)
+#pragma unroll
+      for (int m = 1; m < CPR; m <<= 1) {
+        s0 += __shfl_xor(s0, m);
+        s1 += __shfl_xor(s1, m);
+      }
+      if (r < j.R && c == 0) {
+        const int64_t idx = (int64_t)g * j.R + r;
+        if constexpr (BF) {
+          const bf16 h0 = (bf16)s0, h1 = (bf16)s1;
+          const bf16x4 y = {h0, (bf16)(s0 - (float)h0), h1, (bf16)(s1 - (float)h1)};
+          reinterpret_cast<bf16x4*>(j.out)[idx] = y;
+        } else {
+          reinterpret_cast<f32x2*>(j.out)[idx] = f32x2{s0, s1};
+        }
+      }
+    }
   }
 }
 
@@ -2292,16 +2302,19 @@ hipError_t launch_combine(bool bf, int d, const CombineArgs& a, hipStream_t st) 
 }
 
 hipError_t launch_colc(bool bf, int d, const ColcArgs& a, hipStream_t st) {
-  int64_t rows = 0;
-  for (int jb = 0; jb < a.njobs; ++jb) rows += (int64_t)a.job[jb].G * a.job[jb].R;
-  if (rows == 0) return hipSuccess;
-  const int64_t threads = rows * (d * (bf ? 2 : 4) / 16);  // one lane per 16-byte chunk
-  const int grid = (int)((threads + 255) / 256);
-  if (bf && d == 128) hipLaunchKernelGGL((relattn_colc_kernel<true, 128>), dim3(grid), dim3(256), 0, st, a);
-  else if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), dim3(grid), dim3(256), 0, st, a);
-  else if (bf && d == 32) hipLaunchKernelGGL((relattn_colc_kernel<true, 32>), dim3(grid), dim3(256), 0, st, a);
-  else if (!bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<false, 64>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((relattn_colc_kernel<false, 32>), dim3(grid), dim3(256), 0, st, a);
+  int rmax = 0, gmax = 0;
+  for (int jb = 0; jb < a.njobs; ++jb) {
+    rmax = std::max(rmax, (int)a.job[jb].R);
+    gmax = std::max(gmax, (int)a.job[jb].G);
+  }
+  if (a.njobs == 0 || rmax == 0 || gmax == 0) return hipSuccess;
+  const int rpb = 256 / (d * (bf ? 2 : 4) / 16) * kColcPasses;  // rows per workgroup
+  const dim3 grid((rmax + rpb - 1) / rpb, std::min(gmax, 65535), a.njobs);
+  if (bf && d == 128) hipLaunchKernelGGL((relattn_colc_kernel<true, 128>), grid, dim3(256), 0, st, a);
+  else if (bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<true, 64>), grid, dim3(256), 0, st, a);
+  else if (bf && d == 32) hipLaunchKernelGGL((relattn_colc_kernel<true, 32>), grid, dim3(256), 0, st, a);
+  else if (!bf && d == 64) hipLaunchKernelGGL((relattn_colc_kernel<false, 64>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((relattn_colc_kernel<false, 32>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
