@@ -596,6 +596,24 @@ def test_parity_every_head_with_valid_lengths(wl):
     check_close(got, want, wl.dtype, _case_id(wl))
 
 
+# More (batch, head) groups than the row-constant pass's grid spans in its
+# second dimension (65535): the pass strides its groups over the grid.  Float32
+# DeBERTa and Transformer-XL run the per-key job over B*H = 66000 groups;
+# Transformer-XL's per-distance job runs over H = 33000.  Sampled heads on both
+# sides of the stride.
+@pytest.mark.parametrize("kind", ["deberta", "txl"])
+def test_row_constants_beyond_the_grid_extent(kind):
+    wl = Workload(name="manyheads", kind=kind, B=2, H=33000, Lq=3, Lk=5, d=32, dtype="fp32",
+                  clip_k=4 if kind == "deberta" else 8, causal=kind == "txl",
+                  q_pos_offset=2 if kind == "txl" else 0, table_sigma=0.5)
+    inp = make_inputs(wl, seed=8)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    heads = [(0, 0), (0, 32999), (1, 0), (1, 32534), (1, 32535), (1, 32536), (1, 32999)]
+    want = run_oracle(wl, inp, heads=heads)
+    for i, (b, h) in enumerate(heads):
+        check_close(got[b, h][None], want[i:i + 1], wl.dtype, f"{kind} b{b} h{h}")
+
+
 # ----------------------------------------------------------------------------
 # 4. properties: determinism, masking independence, empty rows, readouts
 # ----------------------------------------------------------------------------
