@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import transformer_attention_relative_amd as ra
+from tests import long_cache
 from transformer_attention_relative_amd.synthetic import WORKLOADS, Workload, make_inputs, params_of
 
 pytestmark = pytest.mark.gpu
@@ -616,66 +617,29 @@ def test_row_constants_beyond_the_grid_extent(kind):
 
 # A key range past 2 GiB per head: the last steps of a decoder over 2^24 +
 # 4109 cached keys, two heads, d = 64 bfloat16, so key rows of head 0 lie past
-# byte 2^31 of K and V and head 1 starts past it.  K = 0 leaves the logit of
-# key j to the relative term alone, and V[j, c] = (((j >> 19) + c) mod 13 +
-# j mod 5) / 64 (exact in bfloat16) changes every 2^19 keys and from one key
-# to the next, so the expected rows reduce to sums of the softmax weights over
-# (j >> 19, j mod 5) classes, computed here in float64 from the oracle's
-# indices.  Head 0 puts almost all weight on the last few keys (rows past
-# 2^31 bytes), head 1 spreads it over the whole range (every split-KV part).
+# byte 2^31 of K and V and head 1 starts past it.  The case and its closed
+# form are in tests/long_cache.py: head 0 puts almost all weight on the last
+# few keys (rows past 2^31 bytes), head 1 spreads it over the whole range
+# (every split-KV part).
 LONG_LK = (1 << 24) + 4109
 LONG_LQ = 2
 
 
 def _long_cache_values(Lk):
+    # long_cache.values, built on the GPU
     j = torch.arange(Lk, dtype=torch.int32, device=DEV)
     c = torch.arange(64, dtype=torch.int32, device=DEV)
     v = ((j >> 19)[:, None] + c[None, :]) % 13 + (j % 5)[:, None]
     return (v.to(torch.float32) / 64).to(torch.bfloat16)
 
 
-def _long_cache_expected(kind, table, qpos, h):
-    Lk = LONG_LK
-    off = np.arange(Lk, dtype=np.int64) - qpos          # key - query (<= 0: causal)
-    vis = off <= 0
-    if kind == "t5":
-        reach = -4096                                     # far past max_distance = 128
-        near = off >= reach
-        bucket = np.empty(Lk, dtype=np.int64)
-        bucket[near] = oracle.t5_bucket_array(off[near], bidirectional=False, num_buckets=32,
-                                              max_distance=128)
-        sat = oracle.t5_bucket(reach - 1, False, 32, 128)
-        assert sat == oracle.t5_bucket(int(off[0]), False, 32, 128)
-        bucket[~near] = sat
-        logit = table[bucket, h].astype(np.float64)
-    else:
-        logit = float(table[h]) * np.abs(off).astype(np.float64)
-    logit = np.where(vis, logit, -np.inf)
-    w = np.exp(logit - logit[vis].max())
-    j = np.arange(Lk, dtype=np.int64)
-    ng = (Lk >> 19) + 1
-    S = np.bincount((j >> 19) * 5 + j % 5, weights=w, minlength=5 * ng).reshape(ng, 5)
-    g = np.arange(ng)[:, None, None]
-    m = np.arange(5)[None, :, None]
-    cc = np.arange(64)[None, None, :]
-    vals = (((g + cc) % 13) + m) / 64.0                 # [group, residue, column]
-    return (S[:, :, None] * vals).sum(axis=(0, 1)) / S.sum()
-
-
 @pytest.mark.parametrize("kind", ["t5", "alibi"])
 def test_key_rows_past_two_gib_per_head(kind):
     Lk, Lq, H = LONG_LK, LONG_LQ, 2
     qpos0 = Lk - Lq                                     # the rows are the last positions
-    if kind == "t5":
-        b = np.arange(32, dtype=np.float64)
-        table = np.stack([np.where(b < 16, 20.0 - 0.5 * b, np.where(b < 31, 4.0 - 0.1 * (b - 16), 0.0)),
-                          np.where(b < 16, 1.0 - 0.05 * b, np.where(b < 31, 0.5 - 0.02 * (b - 16), 0.0))],
-                         axis=1).astype(np.float32)
-    else:
-        table = np.array([-0.5, -2.0 ** -22], dtype=np.float32)
+    table = long_cache.table(kind)
     wl = Workload(name="longcache", kind=kind, B=1, H=H, Lq=Lq, Lk=Lk, d=64, dtype="bf16",
-                  num_buckets=32, max_distance=128, bidirectional=False, causal=True,
-                  q_pos_offset=qpos0)
+                  causal=True, q_pos_offset=qpos0, **long_cache.T5_PARAMS)
     torch.manual_seed(5)
     q = torch.randn(1, H, Lq, 64, device=DEV).to(torch.bfloat16)
     k = torch.zeros(1, H, Lk, 64, dtype=torch.bfloat16, device=DEV)
@@ -683,6 +647,9 @@ def test_key_rows_past_two_gib_per_head(kind):
     v[0, 0] = _long_cache_values(Lk)
     v[0, 1] = v[0, 0]
     assert v[0, 1].data_ptr() - v.data_ptr() > (1 << 31)   # head 1 starts past 2 GiB
+    probe = np.array([0, 1, 4, (1 << 19) - 1, 1 << 19, (1 << 24) - 1, 1 << 24, Lk - 1])
+    assert np.array_equal(v[0, 1, torch.from_numpy(probe).to(DEV)].cpu().double().numpy(),
+                          long_cache.values(probe))
     dev = {"q": q, "k": k, "v": v, "table": torch.from_numpy(table).to(DEV), "table2": None,
            "kv_valid_len": None}
     got = run_gpu(wl, dev).cpu().float().numpy()
@@ -690,7 +657,7 @@ def test_key_rows_past_two_gib_per_head(kind):
     torch.cuda.empty_cache()
     for h in range(H):
         for i in range(Lq):
-            want = _long_cache_expected(kind, table, qpos0 + i, h)
+            want = long_cache.expected(kind, table, Lk, qpos0 + i, h)
             check_close(got[0, h, i][None], want[None], "bf16", f"{kind} h{h} row{i}")
 
 

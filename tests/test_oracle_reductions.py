@@ -13,6 +13,7 @@ import torch
 from hypothesis import given, settings, strategies as st
 
 import oracle
+from tests import long_cache
 
 ATOL = 1e-10
 
@@ -433,3 +434,24 @@ def test_txl_shift_and_table_checks():
         oracle.relattn_forward_head(q, k, v, "txl", 0, enc, uv, q_pos_offset=4)   # not causal
     with pytest.raises(ValueError):
         oracle.relattn_forward_head(q, k, v, "txl", 0, enc[:5], uv, q_pos_offset=4, causal=True)
+
+
+# The long key-cache case of the GPU tests reduces each output row to sums of
+# the softmax weights over (j >> 19, j mod 5) classes; that reduction against
+# the full oracle, at a cache within one class group and one spanning two.
+@pytest.mark.parametrize("Lk", [5000, 600000])
+@pytest.mark.parametrize("kind", ["t5", "alibi"])
+def test_long_cache_closed_form_equals_the_oracle(kind, Lk):
+    tab = long_cache.table(kind)
+    Lq = 2
+    qpos0 = Lk - Lq
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((Lq, long_cache.D))
+    k = np.zeros((Lk, long_cache.D))
+    v = long_cache.values(np.arange(Lk))
+    for h in range(2):
+        want = oracle.relattn_forward_head(q, k, v, kind, h, tab, None, causal=True,
+                                           q_pos_offset=qpos0, **long_cache.T5_PARAMS)
+        for i in range(Lq):
+            got = long_cache.expected(kind, tab, Lk, qpos0 + i, h)
+            assert np.abs(got - want[i]).max() < 1e-12, (kind, Lk, h, i)
