@@ -574,6 +574,42 @@ def test_parity_full_size_sampled(name):
             check_close(got[b, h][rows][None], want, wl.dtype, f"{name} b{b} h{h}")
 
 
+# Long sequences, every kind: 65573 positions (70001 for DeBERTa k = 512, a
+# 4096-token Transformer-XL segment over 65573 keys), two heads, sampled rows
+# of both; tile, ring and table indices far past the benchmark's lengths.
+LONG_CASES = [
+    Workload(name="long", kind="t5", B=1, H=2, Lq=65573, Lk=65573, d=64, dtype="bf16",
+             num_buckets=32, max_distance=128, bidirectional=True, table_sigma=0.5),
+    Workload(name="long", kind="shaw", B=1, H=2, Lq=65573, Lk=65573, d=64, dtype="bf16",
+             clip_k=16, causal=True, table_sigma=0.1),
+    Workload(name="long", kind="deberta", B=1, H=2, Lq=70001, Lk=70001, d=64, dtype="bf16",
+             clip_k=512, table_sigma=0.1),
+    Workload(name="long", kind="alibi", B=1, H=2, Lq=65573, Lk=65573, d=64, dtype="bf16",
+             causal=True, table_sigma=0.1),
+    Workload(name="long", kind="txl", B=1, H=2, Lq=4096, Lk=65573, d=64, dtype="bf16",
+             clip_k=65573, q_pos_offset=65573 - 4096, causal=True, table_sigma=0.1),
+]
+
+
+@pytest.mark.parametrize("wl", LONG_CASES, ids=lambda w: f"{w.kind}-Lq{w.Lq}-Lk{w.Lk}")
+def test_parity_long_sequences_sampled(wl):
+    inp = make_inputs(wl, seed=4)
+    # sharper attention than the default inputs give over this many keys, so
+    # the rows are not near-uniform averages of V (DeBERTa's scale is the
+    # smallest, 1/sqrt(3d))
+    inp["q"] = (inp["q"].float() * (6 if wl.kind == "deberta" else 3)).to(inp["q"].dtype)
+    got = run_gpu(wl, _to_dev(inp)).cpu().float().numpy()
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(4)
+    q, k, v = _np(inp["q"]), _np(inp["k"]), _np(inp["v"])
+    t1, t2 = _np(inp["table"]), _np(inp["table2"])
+    for h in range(wl.H):
+        rows = _sample_rows(wl.Lq, rng)
+        want = oracle.relattn_forward(q, k, v, wl.kind, t1, t2, heads=[(0, h)], rows=rows,
+                                      **params_of(wl))
+        check_close(got[0, h][rows][None], want, wl.dtype, f"long {wl.kind} h{h}")
+
+
 # Per-sequence valid lengths without a causal mask: the kernel orders its
 # work by sequence length and rearranges dispatch positions (384 and 400
 # workgroups here: 48 and 50 per XCD, two per CU), so every head and every
