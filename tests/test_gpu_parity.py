@@ -577,6 +577,8 @@ def test_parity_full_size_sampled(name):
 # Long sequences, every kind: 65573 positions (70001 for DeBERTa k = 512, a
 # 4096-token Transformer-XL segment over 65573 keys), two heads, sampled rows
 # of both; tile, ring and table indices far past the benchmark's lengths.
+# The other kernel templates (128- and 32-wide heads, float32) at 30011 and
+# 8191 positions.
 LONG_CASES = [
     Workload(name="long", kind="t5", B=1, H=2, Lq=65573, Lk=65573, d=64, dtype="bf16",
              num_buckets=32, max_distance=128, bidirectional=True, table_sigma=0.5),
@@ -588,10 +590,23 @@ LONG_CASES = [
              causal=True, table_sigma=0.1),
     Workload(name="long", kind="txl", B=1, H=2, Lq=4096, Lk=65573, d=64, dtype="bf16",
              clip_k=65573, q_pos_offset=65573 - 4096, causal=True, table_sigma=0.1),
+    # the other kernel templates: 128- and 32-wide heads, float32
+    Workload(name="long", kind="alibi", B=1, H=2, Lq=30011, Lk=30011, d=128, dtype="bf16",
+             causal=True, table_sigma=0.1),
+    Workload(name="long", kind="deberta", B=1, H=2, Lq=30011, Lk=30011, d=128, dtype="bf16",
+             clip_k=512, table_sigma=0.1),
+    Workload(name="long", kind="txl", B=1, H=2, Lq=2048, Lk=30011, d=128, dtype="bf16",
+             clip_k=30011, q_pos_offset=30011 - 2048, causal=True, table_sigma=0.1),
+    Workload(name="long", kind="shaw", B=1, H=2, Lq=30011, Lk=30011, d=32, dtype="bf16",
+             clip_k=32, causal=False, table_sigma=0.1),
+    Workload(name="long", kind="t5", B=1, H=2, Lq=8191, Lk=8191, d=64, dtype="fp32",
+             num_buckets=32, max_distance=128, bidirectional=False, causal=True, table_sigma=0.5),
+    Workload(name="long", kind="deberta", B=1, H=2, Lq=8191, Lk=8191, d=32, dtype="fp32",
+             clip_k=256, table_sigma=0.1),
 ]
 
 
-@pytest.mark.parametrize("wl", LONG_CASES, ids=lambda w: f"{w.kind}-Lq{w.Lq}-Lk{w.Lk}")
+@pytest.mark.parametrize("wl", LONG_CASES, ids=lambda w: f"{w.kind}-{w.dtype}-d{w.d}-Lq{w.Lq}-Lk{w.Lk}")
 def test_parity_long_sequences_sampled(wl):
     inp = make_inputs(wl, seed=4)
     # sharper attention than the default inputs give over this many keys, so
