@@ -97,6 +97,23 @@ def test_fwd_validation_rejects_before_launch(lib, kw, status):
     assert lib.relattn_last_error().decode() != ""
 
 
+# sizes past what the kernels index with 32-bit integers or build for: the
+# status says unsupported and the message names the limit
+@pytest.mark.parametrize("kw,reason", [
+    (dict(kind="t5", table=FAKE, q_pos_offset=(1 << 28) - 10), "query positions above 2^28"),
+    (dict(kind="t5", table=FAKE, k_pos_offset=(1 << 28) - 10), "key positions above 2^28"),
+    (dict(kind="t5", table=FAKE, B=1 << 12, H=(1 << 12) + 1), "B*H too large"),
+    (dict(kind="t5", table=FAKE, Lq=(1 << 26) + 1), "sequence length above 2^26"),
+    (dict(kind="t5", table=FAKE, Lk=(1 << 26) + 1), "sequence length above 2^26"),
+    (dict(kind="t5", table=FAKE, B=1 << 12, H=1 << 12, Lq=1 << 26), "grid too large"),
+    (dict(kind="deberta", table=FAKE, table2=FAKE, clip_k=65537), "above 65536"),
+])
+def test_fwd_rejects_sizes_past_the_limits(lib, kw, reason):
+    p = _params(**kw)
+    assert _fwd_status(lib, p) == 2
+    assert reason in lib.relattn_last_error().decode()
+
+
 def test_fwd_rejects_bad_kind_and_dtype(lib):
     p = _params(table=FAKE)
     p.kind = 7
