@@ -1392,6 +1392,10 @@ void relattn_fwd_kernel(FwdArgs a) {
           // (q + v).E[i - j] for the block's 63 distances by MFMA (rows
           // E[T0 + m], columns = queries), stored [query][m] in the wave's
           // LDS tile and read back along each query's diagonal
+          // the band's MFMAs and stores at raised wave priority in the
+          // eight-wave kernel (see DeBERTa below; Transformer-XL with
+          // memory 288.4 -> 278.3 us)
+          if constexpr (KR_RING) __builtin_amdgcn_s_setprio(2);
           float* band = relf + wave * L.deb_wave_floats;
           const T* enc = reinterpret_cast<const T*>(a.table);
           const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
@@ -1440,6 +1444,7 @@ void relattn_fwd_kernel(FwdArgs a) {
               *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
             }
           }
+          if constexpr (KR_RING) __builtin_amdgcn_s_setprio(0);
           wave_lds_fence();
           f32x16 init;
           {
@@ -1464,6 +1469,13 @@ void relattn_fwd_kernel(FwdArgs a) {
             // one 32 x kCbandStride float tile per wave, used first for the
             // content-to-position band, then for the position-to-content band
             float* band = relf + wave * L.deb_wave_floats;
+            // In the eight-wave kernel the content-to-position band's MFMAs
+            // and stores run at raised wave priority: they start the
+            // block's dependency chain, and the other wave of the SIMD fills
+            // in behind them (k=512: 268.4 -> 261.5 us; keeping the priority
+            // through the position-to-content band as well gains nothing,
+            // 267.9 us)
+            if constexpr (KR_RING) __builtin_amdgcn_s_setprio(2);
             const T* kr = reinterpret_cast<const T*>(a.table);
             const T* qr = reinterpret_cast<const T*>(a.table2);
             const int T0 = pq_min - j0 - 31;  // band index m <-> query - key = T0 + m
@@ -1497,6 +1509,7 @@ void relattn_fwd_kernel(FwdArgs a) {
                 *reinterpret_cast<f32x4*>(dst + 8 * g) = x;
               }
             }
+            if constexpr (KR_RING) __builtin_amdgcn_s_setprio(0);
             wave_lds_fence();
             // key j0 + jl of query row lq sits at m = lq - jl + 31
             float cg[16];
